@@ -1,0 +1,380 @@
+"""Benchmark of the paged decoder-attention core on one MI355X.
+
+    python bench.py [--steps K] [--warmup W] [--workload qwen3|mistral|llama31|phi3] [--no-cpu-baseline]
+
+A step is one pass of the whole path over one batch of synthetic input,
+resident in HBM before timing starts. The default workload is the
+Qwen3-4B-shaped step_paged pass (QK-norm, rope, the page write of 2176
+tokens, packed prefill of 2048 tokens from 8 prompts, 4 of which share a
+128-token prefix through shared pages, and the split decode of 128 rows at
+positions U[512, 40960)), the one configuration that runs every stage.
+Other workloads: mistral (64-row decode, contexts U[1024, 32768]), llama31
+(8192-token chunk at 57344..65535 with llama3 rope), phi3 (4 packed prompts,
+window 2047, then the 4-row decode at position 3000).
+
+Prints ONE JSON line. value = algorithmic bytes of the step / step time
+(GB/s); the roofline object covers the kernel with the most time, timed with
+HIP events recorded by the library around every launch on the launch stream
+during a second timed pass; cpu_baseline times the fp64 oracle on a bounded
+sample of the same workload on this host.
+"""
+import argparse
+import hashlib
+import json
+import os
+import sys
+import time
+
+import numpy as np
+import torch
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+import decoder_attention_paged_amd as dap  # noqa: E402
+import workloads as W  # noqa: E402
+
+HBM_PEAK_GBS = 8000.0          # MI355X HBM3E, vendor figure
+BF16_PEAK_TFLOPS = 2500.0      # MI355X dense bf16 MFMA, vendor figure
+METRIC = "decode_paged attn GB/s (% HBM peak); prefill_packed attn TFLOP/s (% MFMA)"
+PROFILES = os.path.join(ROOT, "profiles")
+
+
+def i32(a):
+    return torch.as_tensor(np.ascontiguousarray(a, dtype=np.int32), device="cuda")
+
+
+def key_counts(positions, window):
+    p = np.asarray(positions, dtype=np.int64)
+    lo = np.maximum(0, p - window + 1) if window > 0 else np.zeros_like(p)
+    return p - lo + 1, lo
+
+
+def decode_bytes(m, positions):
+    """HBM bytes a decode must move: each attended K and V element once per kv
+    head (shared by the g query heads), q in, out, and the table entries read."""
+    n, lo = key_counts(positions, m.window)
+    pages = np.asarray(positions) // 64 - lo // 64 + 1
+    R = len(positions)
+    return int(np.sum(n) * m.n_kv_heads * m.head_dim * 2 * 2 + R * m.n_q_heads * m.head_dim * 2 * 2
+               + np.sum(pages) * 4)
+
+
+def write_bytes(m, T):
+    """Read the fused q,k,v rows; write q_out, K and V."""
+    return int(T * m.qkv_width * 2 * 2)
+
+
+def prefill_flops(m, positions):
+    n, _ = key_counts(positions, m.window)
+    return float(4.0 * m.head_dim * m.n_q_heads * np.sum(n))
+
+
+def prefill_bytes(m, positions, segments):
+    """q in, out, and each row's attended K/V once."""
+    T = len(positions)
+    b = T * m.n_q_heads * m.head_dim * 2 * 2
+    for r in np.unique(segments):
+        pr = np.asarray(positions)[np.asarray(segments) == r]
+        lo = max(0, int(pr.min()) - m.window + 1) if m.window > 0 else 0
+        b += (int(pr.max()) - lo + 1) * m.n_kv_heads * m.head_dim * 2 * 2
+    return int(b)
+
+
+class Bench:
+    """Inputs resident on the GPU plus the step function of one workload."""
+
+    def __init__(self, name):
+        self.name = name
+        self.wl = W.ALL[name]()
+        wl, m = self.wl, self.wl.model
+        self.m = m
+        self.h = dap.Handle(dap.Model(m.n_q_heads, m.n_kv_heads, m.head_dim, m.rope_theta, window=m.window,
+                                      max_position=m.max_position, llama3=m.llama3, qk_norm_eps=m.qk_norm_eps))
+        self.kp, self.vp = dap.pools(wl.n_pages, m.n_kv_heads, m.head_dim)
+        for s in range(0, wl.n_pages, 2048):
+            ids = np.arange(s, min(s + 2048, wl.n_pages))
+            dap.store_pages(self.kp, self.vp, ids, wl.pages("k", ids, "cuda"), wl.pages("v", ids, "cuda"))
+        self.table = i32(wl.table)
+        D, hq, hkv = m.head_dim, m.n_q_heads, m.n_kv_heads
+        self.gains = (wl.gains("q", "cuda"), wl.gains("k", "cuda")) if m.qk_norm_eps else (None, None)
+        if name == "qwen3":
+            P, R = wl.n_pre, wl.n_dec
+            self.qkv = wl.qkv("step", P + R, "cuda")
+            self.pos_np = np.concatenate([wl.pre_positions, wl.dec_positions])
+            self.rows_np = np.concatenate([wl.pre_segments, wl.dec_rows])
+            self.pos, self.rows = i32(self.pos_np), i32(self.rows_np)
+            self.q_out = torch.empty(P + R, hq * D, dtype=torch.int16, device="cuda")
+            self.out = torch.empty_like(self.q_out)
+            self.ws = self.h.workspace(self.h.step_workspace_bytes(P, 8, R))
+            self.bytes = (write_bytes(m, P + R) + decode_bytes(m, wl.dec_positions)
+                          + prefill_bytes(m, wl.pre_positions, wl.pre_segments))
+            self.flops = prefill_flops(m, wl.pre_positions)
+            self.dec_bytes = decode_bytes(m, wl.dec_positions)
+            self.tokens = P + R
+            self.desc = ("qwen3-4b-shaped step_paged: 2048 packed prefill tokens (8 prompts of 256, 4 sharing a "
+                         "128-token prefix via shared pages) + 128 decode rows at p~U[512,40959], Hq32/Hkv8/D128, "
+                         "QK-norm eps 1e-6, theta 1e6, page 64")
+        elif name == "mistral":
+            R = wl.n_dec
+            self.qkv = wl.qkv("step", R, "cuda")
+            self.pos, self.rows = i32(wl.dec_positions), i32(wl.dec_rows)
+            self.q_out = torch.empty(R, hq * D, dtype=torch.int16, device="cuda")
+            self.out = torch.empty_like(self.q_out)
+            self.ws = self.h.workspace(self.h.decode_workspace_bytes(R))
+            self.dec_bytes = decode_bytes(m, wl.dec_positions)
+            self.bytes = write_bytes(m, R) + self.dec_bytes
+            self.flops = 0.0
+            self.tokens = R
+            self.desc = "mistral-7b-shaped decode_paged: 64 rows, contexts U[1024,32768], Hq32/Hkv8/D128, page 64"
+        elif name == "llama31":
+            T = wl.n_pre
+            self.qkv = wl.qkv("chunk", T, "cuda")
+            self.pos, self.seg = i32(wl.pre_positions), i32(wl.pre_segments)
+            self.q_out = torch.empty(T, hq * D, dtype=torch.int16, device="cuda")
+            self.out = torch.empty_like(self.q_out)
+            self.ws = self.h.workspace(self.h.prefill_workspace_bytes(T, 1))
+            self.flops = prefill_flops(m, wl.pre_positions)
+            self.bytes = write_bytes(m, T) + prefill_bytes(m, wl.pre_positions, wl.pre_segments)
+            self.dec_bytes = 0
+            self.tokens = T
+            self.desc = ("llama-3.1-8b-shaped chunked prefill: 8192 tokens at 57344..65535 over a paged 65536 "
+                         "prefix, Hq32/Hkv8/D128, theta 5e5 + llama3 (8,1,4,8192)")
+        elif name == "phi3":
+            T = wl.n_pre
+            self.qkv = wl.qkv("prompt", T, "cuda")
+            self.pos, self.seg = i32(wl.pre_positions), i32(wl.pre_segments)
+            self.q_out = torch.empty(T, hq * D, dtype=torch.int16, device="cuda")
+            self.out = torch.empty_like(self.q_out)
+            self.ws_p = self.h.workspace(self.h.prefill_workspace_bytes(T, 4))
+            self.dq = W.normal_matrix(wl.key("q", "final"), 4, hq * D, "cuda")
+            self.dpos = i32(np.full(4, 3000))
+            self.dout = torch.empty(4, hq * D, dtype=torch.int16, device="cuda")
+            self.ws = self.h.workspace(self.h.decode_workspace_bytes(4))
+            self.dec_bytes = decode_bytes(m, np.full(4, 3000))
+            self.flops = prefill_flops(m, wl.pre_positions)
+            self.bytes = (write_bytes(m, T) + prefill_bytes(m, wl.pre_positions, wl.pre_segments)
+                          + self.dec_bytes)
+            self.tokens = T + 4
+            self.desc = ("phi-3-mini-shaped: prefill_packed of 4096 tokens (prompts 512/1024/1536/1024, window "
+                         "2047, Hq=Hkv=32, D96) then decode_paged of the 4 rows at position 3000")
+        else:
+            raise SystemExit(f"unknown workload {name}")
+        D = m.head_dim
+        self.split = (self.qkv[:, :hq * D], self.qkv[:, hq * D:(hq + hkv) * D], self.qkv[:, (hq + hkv) * D:])
+        torch.cuda.synchronize()
+
+    def step(self):
+        h, m, wl = self.h, self.m, self.wl
+        if self.name == "qwen3":
+            h.step_paged(*self.split, self.pos, self.rows, self.table, self.kp, self.vp, n_prompt=wl.n_pre,
+                         n_segments=8, q_gain=self.gains[0], k_gain=self.gains[1], q_out=self.q_out, out=self.out,
+                         workspace=self.ws)
+        elif self.name == "mistral":
+            h.rope_qknorm_write_pages(*self.split, self.pos, self.kp, self.vp, rows=self.rows, table=self.table,
+                                      q_out=self.q_out)
+            h.attn_decode_paged(self.q_out, self.pos, self.table, self.kp, self.vp, out=self.out, workspace=self.ws)
+        elif self.name == "llama31":
+            h.rope_qknorm_write_pages(*self.split, self.pos, self.kp, self.vp, rows=self.seg, table=self.table,
+                                      q_out=self.q_out)
+            h.attn_prefill_packed(self.q_out, self.pos, self.seg, self.table, self.kp, self.vp, n_segments=1,
+                                  out=self.out, workspace=self.ws)
+        elif self.name == "phi3":
+            h.rope_qknorm_write_pages(*self.split, self.pos, self.kp, self.vp, rows=self.seg, table=self.table,
+                                      q_out=self.q_out)
+            h.attn_prefill_packed(self.q_out, self.pos, self.seg, self.table, self.kp, self.vp, n_segments=4,
+                                  out=self.out, workspace=self.ws_p)
+            h.attn_decode_paged(self.dq, self.dpos, self.table, self.kp, self.vp, out=self.dout, workspace=self.ws)
+
+
+# --------------------------------------------------------------------------- CPU baseline
+def cpu_baseline(b: Bench, budget_s: float = 20.0):
+    """The fp64 oracle as it stands, on a bounded sample of the same workload."""
+    from oracle import attention, bf16, core, pages, rope
+
+    try:
+        from threadpoolctl import threadpool_info
+        threads = max([i.get("num_threads", 1) for i in threadpool_info()] or [1])
+    except Exception:  # pragma: no cover
+        threads = 1
+    wl, m = b.wl, b.m
+    freqs = rope.inv_freq(m.rope_theta, m.head_dim, m.llama3)
+    gains = None
+    if m.qk_norm_eps:
+        gains = tuple(g.cpu().numpy().view(np.uint16) for g in b.gains)
+    # the sample: every token's front half (write), a few prompts / decode rows
+    if b.name == "qwen3":
+        tok_pos, tok_rows = b.pos_np, b.rows_np
+        pre_pick = np.nonzero(np.isin(wl.pre_segments, [0, 4]))[0]
+        dec_pick = np.arange(8)
+    elif b.name == "mistral":
+        tok_pos, tok_rows = wl.dec_positions, wl.dec_rows
+        pre_pick = np.zeros(0, int)
+        dec_pick = np.arange(8)
+    else:
+        tok_pos, tok_rows = wl.pre_positions, wl.pre_segments
+        pre_pick = np.arange(0, wl.n_pre, max(1, wl.n_pre // (64 if b.name == "llama31" else 512)))
+        dec_pick = np.zeros(0, int)
+    qkv_np = b.qkv.cpu().numpy().view(np.uint16)
+    # pages the sample reads, generated before timing (input generation is not the oracle)
+    need = set()
+    for r, p in list(zip(wl.pre_segments[pre_pick], wl.pre_positions[pre_pick])) + \
+            list(zip(wl.dec_rows[dec_pick] if len(wl.dec_rows) else [], wl.dec_positions[dec_pick]
+                     if len(wl.dec_positions) else [])):
+        lo = max(0, p - m.window + 1) if m.window > 0 else 0
+        need.update(int(x) for x in wl.table[r, lo // 64: p // 64 + 1])
+    need = sorted(need)
+    cache = {}
+    for s in range(0, len(need), 1024):
+        part = need[s:s + 1024]
+        k = wl.pages("k", part, "cuda").cpu().numpy().view(np.uint16)
+        v = wl.pages("v", part, "cuda").cpu().numpy().view(np.uint16)
+        for j, pg in enumerate(part):
+            cache[pg] = (k[j], v[j])
+
+    t0 = time.perf_counter()
+    q, k, vb = core.prepare_tokens(qkv_np, tok_pos, m.n_q_heads, m.n_kv_heads, m.head_dim, freqs,
+                                   gains[0] if gains else None, gains[1] if gains else None, m.qk_norm_eps)
+    q_bits, k_bits = bf16.from_f64(q), bf16.from_f64(k)
+    slots = pages.slot_of(wl.table, tok_rows, tok_pos)
+    written = {}
+    for t, s in enumerate(slots):
+        written.setdefault(int(s) // 64, []).append((int(s) % 64, t))
+    pages_f64 = {}
+
+    def read_page(pg):
+        if pg not in pages_f64:
+            kk, vv = cache[pg]
+            kk, vv = kk.copy(), vv.copy()
+            for i, t in written.get(pg, []):
+                kk[:, i] = k_bits[t]
+                vv[:, i] = vb[t]
+            pages_f64[pg] = (bf16.to_f64(kk), bf16.to_f64(vv))
+        return pages_f64[pg]
+
+    qf = bf16.to_f64(q_bits)
+    done_bytes = write_bytes(m, len(tok_pos))
+    if len(pre_pick):
+        attention.paged(qf[pre_pick], wl.pre_positions[pre_pick], wl.pre_segments[pre_pick], wl.table, read_page,
+                        m.window)
+        done_bytes += prefill_bytes(m, wl.pre_positions[pre_pick], wl.pre_segments[pre_pick])
+    if len(dec_pick):
+        off = wl.n_pre if b.name == "qwen3" else 0
+        attention.paged(qf[off + dec_pick], wl.dec_positions[dec_pick], wl.dec_rows[dec_pick], wl.table,
+                        read_page, m.window)
+        done_bytes += decode_bytes(m, wl.dec_positions[dec_pick])
+    dt = time.perf_counter() - t0
+    sample = (f"oracle front half (norm/rope/round/slots) of all {len(tok_pos)} tokens, prefill of "
+              f"{len(pre_pick)} tokens, decode of {len(dec_pick)} rows; {done_bytes / 1e9:.3f} GB of algorithmic "
+              f"traffic in {dt:.1f} s; host {os.cpu_count()} CPUs visible")
+    return {"value": round(done_bytes / dt / 1e9, 4), "unit": "GB/s", "cores": int(threads), "kind": "oracle",
+            "sample": sample, "seconds": round(dt, 2)}
+
+
+# --------------------------------------------------------------------------- traffic counters
+def traffic_for(kernel: str, workload: str):
+    """HBM bytes per launch from the committed rocprofv3 counter summary,
+    null when absent or taken on a different kernel source."""
+    path = os.path.join(PROFILES, f"{kernel}_{workload}_counters.json")
+    if not os.path.exists(path):
+        return None
+    with open(path) as fh:
+        rec = json.load(fh)
+    src = os.path.join(ROOT, "decoder_attention_paged_amd", "csrc", rec.get("source", ""))
+    if not os.path.exists(src):
+        return None
+    digest = hashlib.sha256(open(src, "rb").read()).hexdigest()
+    if digest != rec.get("source_sha256"):
+        return None
+    return rec.get("bytes_per_launch")
+
+
+def main():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=20)
+    ap.add_argument("--warmup", type=int, default=3)
+    ap.add_argument("--workload", default="qwen3", choices=["qwen3", "mistral", "llama31", "phi3"])
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    args = ap.parse_args()
+    if args.gpus != 1:
+        print(f"bench.py runs on one GPU only: this build has no multi-GPU path (asked for --gpus {args.gpus}); "
+              "the core would shard by kv head with no exchange, see the design notes", file=sys.stderr)
+        sys.exit(2)
+    if not torch.cuda.is_available():
+        print("bench.py needs a GPU", file=sys.stderr)
+        sys.exit(1)
+    torch.cuda.set_device(0)
+    b = Bench(args.workload)
+    for _ in range(args.warmup):
+        b.step()
+    torch.cuda.synchronize()
+
+    # timed pass: wall clock and stream events around exactly K steps
+    start, stop = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    start.record()
+    for _ in range(args.steps):
+        b.step()
+    stop.record()
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+    ms_per_step = wall * 1e3 / args.steps
+
+    # second timed pass with the library's per-launch events
+    b.h.set_profiling(True)
+    b.h.profile_read(reset=True)
+    for _ in range(args.steps):
+        b.step()
+    torch.cuda.synchronize()
+    prof = b.h.profile_read(reset=True)
+    b.h.set_profiling(False)
+    kern_ms = {k: (v[0] / v[1] if v[1] else 0.0) for k, v in prof.items()}
+
+    m = b.m
+    value = b.bytes / (ms_per_step * 1e-3) / 1e9
+    dom = max(("decode", "prefill", "write"), key=lambda k: prof[k][0])
+    if dom == "decode":
+        per_launch = b.dec_bytes
+        achieved = per_launch / (kern_ms["decode"] * 1e-3) / 1e9
+        roof = {"bound": "hbm", "achieved": round(achieved, 2), "peak": HBM_PEAK_GBS, "unit": "GB/s",
+                "frac": round(achieved / HBM_PEAK_GBS, 4), "kernel": "decode_kernel",
+                "avg_launch_ms": round(kern_ms["decode"], 5), "algorithmic_bytes_per_launch": per_launch}
+    elif dom == "prefill":
+        achieved = b.flops / (kern_ms["prefill"] * 1e-3) / 1e12
+        roof = {"bound": "mfma", "achieved": round(achieved, 2), "peak": BF16_PEAK_TFLOPS, "unit": "TFLOP/s",
+                "frac": round(achieved / BF16_PEAK_TFLOPS, 4), "kernel": "prefill_kernel",
+                "avg_launch_ms": round(kern_ms["prefill"], 5), "algorithmic_flops_per_launch": b.flops}
+    else:
+        per_launch = write_bytes(m, b.tokens)
+        achieved = per_launch / (kern_ms["write"] * 1e-3) / 1e9
+        roof = {"bound": "hbm", "achieved": round(achieved, 2), "peak": HBM_PEAK_GBS, "unit": "GB/s",
+                "frac": round(achieved / HBM_PEAK_GBS, 4), "kernel": "rope_write_kernel",
+                "avg_launch_ms": round(kern_ms["write"], 5)}
+    roof["traffic"] = traffic_for(roof["kernel"], args.workload)
+
+    line = {
+        "metric": METRIC, "value": round(value, 2), "unit": "GB/s", "n_gpus": 1, "steps": args.steps,
+        "warmup": args.warmup, "ms_per_step": round(ms_per_step, 4), "higher_is_better": True,
+        "scaling": "weak", "vs_baseline": None, "dtype": "bf16", "data": "synthetic",
+        "config": {"workload": b.desc, "parallelism": "single GPU"},
+        "roofline": roof,
+        "event_ms_per_step": round(start.elapsed_time(stop) / args.steps, 4),
+        "tokens_per_s": round(b.tokens / (ms_per_step * 1e-3), 1),
+        "kernel_avg_ms": {k: round(v, 5) for k, v in kern_ms.items() if prof[k][1]},
+    }
+    if b.flops:
+        line["prefill_tflops"] = round(b.flops / (kern_ms["prefill"] * 1e-3) / 1e12, 2)
+        line["prefill_frac_of_mfma_peak"] = round(line["prefill_tflops"] / BF16_PEAK_TFLOPS, 4)
+    if b.dec_bytes:
+        g = b.dec_bytes / (kern_ms["decode"] * 1e-3) / 1e9
+        line["decode_gbps"] = round(g, 2)
+        line["decode_frac_of_hbm_peak"] = round(g / HBM_PEAK_GBS, 4)
+    if not args.no_cpu_baseline:
+        line["cpu_baseline"] = cpu_baseline(b)
+    print(json.dumps(line), flush=True)
+
+
+if __name__ == "__main__":
+    main()

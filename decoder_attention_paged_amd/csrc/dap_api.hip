@@ -1,0 +1,539 @@
+// C-ABI layer: handle, argument checks, validate mode, launches.
+#include <cmath>
+#include <cstdio>
+#include <cstring>
+#include <string>
+#include <unordered_set>
+#include <vector>
+
+#include "dap_internal.h"
+
+// ---------------------------------------------------------------- kernel timing
+namespace dap {
+
+struct ProfilerState {
+    static constexpr int kCap = 1024;
+    std::vector<hipEvent_t> start, stop;
+    std::vector<int> kind;
+    int head = 0, count = 0, cur = -1;
+    double total_ms[DAP_N_KERNELS] = {};
+    int64_t launches[DAP_N_KERNELS] = {};
+
+    hipError_t init() {
+        start.assign(kCap, nullptr);
+        stop.assign(kCap, nullptr);
+        kind.assign(kCap, 0);
+        for (int i = 0; i < kCap; ++i) {
+            hipError_t e = hipEventCreate(&start[i]);
+            if (e == hipSuccess) e = hipEventCreate(&stop[i]);
+            if (e != hipSuccess) return e;
+        }
+        return hipSuccess;
+    }
+    ~ProfilerState() {
+        for (auto ev : start) if (ev) (void)hipEventDestroy(ev);
+        for (auto ev : stop) if (ev) (void)hipEventDestroy(ev);
+    }
+    hipError_t drain_one() {
+        const int i = head;
+        float ms = 0.f;
+        hipError_t e = hipEventSynchronize(stop[i]);
+        if (e == hipSuccess) e = hipEventElapsedTime(&ms, start[i], stop[i]);
+        if (e != hipSuccess) return e;
+        total_ms[kind[i]] += ms;
+        launches[kind[i]] += 1;
+        head = (head + 1) % kCap;
+        --count;
+        return hipSuccess;
+    }
+};
+
+void Profiler::begin(int k, hipStream_t s) {
+    if (st->count == ProfilerState::kCap) (void)st->drain_one();
+    const int i = (st->head + st->count) % ProfilerState::kCap;
+    st->kind[i] = k;
+    st->cur = i;
+    (void)hipEventRecord(st->start[i], s);
+}
+
+void Profiler::end(int, hipStream_t s) {
+    if (st->cur < 0) return;
+    (void)hipEventRecord(st->stop[st->cur], s);
+    st->cur = -1;
+    st->count += 1;
+}
+
+}  // namespace dap
+
+struct dap_handle {
+    dap_model m;
+    int device;
+    int group;
+    std::vector<double> h_inv_freq;
+    double* d_inv_freq;
+    unsigned* d_err;
+    int validate;
+    dap::ProfilerState* prof_state;
+    dap::Profiler prof;
+    dap::Profiler* profiler() { return prof_state ? &prof : nullptr; }
+};
+
+namespace {
+
+thread_local std::string g_last_error;
+
+int fail(int code, const std::string& msg) {
+    g_last_error = msg;
+    return code;
+}
+
+int hip_fail(hipError_t e, const char* what) {
+    return fail(DAP_HIP_ERROR, std::string(what) + ": " + hipGetErrorString(e));
+}
+
+bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
+bool aligned4(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 3u) == 0; }
+
+#define DAP_REQUIRE(cond, code, msg) \
+    do {                             \
+        if (!(cond)) return fail((code), (msg)); \
+    } while (0)
+
+// Frequency table in float64 (see dap_create in dap.h).
+std::vector<double> build_inv_freq(const dap_model& m) {
+    const int half = m.head_dim / 2;
+    std::vector<double> f(half);
+    for (int i = 0; i < half; ++i) f[i] = std::pow(m.rope_theta, -2.0 * i / m.head_dim);
+    if (m.llama3) {
+        const double factor = m.llama3_factor, low = m.llama3_low_freq_factor, high = m.llama3_high_freq_factor;
+        const double orig = m.llama3_original_max_position;
+        const double low_wavelen = orig / low, high_wavelen = orig / high;
+        for (int i = 0; i < half; ++i) {
+            const double wavelen = 2.0 * M_PI / f[i];
+            if (wavelen < high_wavelen) continue;
+            if (wavelen > low_wavelen) {
+                f[i] = f[i] / factor;
+            } else {
+                const double s = (orig / wavelen - low) / (high - low);
+                f[i] = (1.0 - s) * f[i] / factor + s * f[i];
+            }
+        }
+    }
+    return f;
+}
+
+// ---------------------------------------------------------------- validate mode
+template <typename T>
+bool to_host(std::vector<T>& dst, const T* src, size_t n, hipStream_t s) {
+    dst.resize(n);
+    if (n == 0) return true;
+    if (hipMemcpyAsync(dst.data(), src, n * sizeof(T), hipMemcpyDeviceToHost, s) != hipSuccess) return false;
+    return hipStreamSynchronize(s) == hipSuccess;
+}
+
+int begin_validate(dap_handle* h, hipStream_t s) {
+    hipError_t e = hipMemsetAsync(h->d_err, 0, sizeof(unsigned), s);
+    if (e != hipSuccess) return hip_fail(e, "hipMemsetAsync(error word)");
+    return DAP_OK;
+}
+
+int end_validate(dap_handle* h, hipStream_t s) {
+    unsigned err = 0;
+    hipError_t e = hipMemcpyAsync(&err, h->d_err, sizeof(unsigned), hipMemcpyDeviceToHost, s);
+    if (e == hipSuccess) e = hipStreamSynchronize(s);
+    if (e != hipSuccess) return hip_fail(e, "reading the error word");
+    if (err) {
+        char buf[160];
+        std::snprintf(buf, sizeof buf, "a kernel skipped out-of-range index entries (error bits 0x%x: 1 position, 2 row, "
+                      "4 page, 8 slot, 16 table width, 32 segment runs)", err);
+        return fail(DAP_BAD_INDEX, buf);
+    }
+    return DAP_OK;
+}
+
+// Host checks of (row, position) -> page through the table; returns DAP_OK or DAP_BAD_INDEX.
+int check_rows(const dap_handle* h, const std::vector<int32_t>& pos, const std::vector<int32_t>& rows,
+               const std::vector<int32_t>& table, int32_t table_ld, int32_t n_table_rows, int32_t n_pages,
+               bool whole_range, std::vector<long long>* slots_out) {
+    const int W = h->m.window;
+    for (size_t t = 0; t < pos.size(); ++t) {
+        const int p = pos[t];
+        if (p < 0 || p >= h->m.max_position) return fail(DAP_BAD_INDEX, "position " + std::to_string(p) + " out of range at " + std::to_string(t));
+        const int r = rows.empty() ? (int)t : rows[t];
+        if (r < 0 || r >= n_table_rows) return fail(DAP_BAD_INDEX, "table row " + std::to_string(r) + " out of range at " + std::to_string(t));
+        const int lo = whole_range ? (W > 0 ? std::max(0, p - W + 1) : 0) : p;
+        if (p / dap::kPage >= table_ld) return fail(DAP_BAD_INDEX, "position beyond the table width at " + std::to_string(t));
+        for (int j = lo / dap::kPage; j <= p / dap::kPage; ++j) {
+            const int pg = table[(size_t)r * table_ld + j];
+            if (pg < 0 || pg >= n_pages) return fail(DAP_BAD_INDEX, "page id " + std::to_string(pg) + " out of range (row " + std::to_string(r) + ", entry " + std::to_string(j) + ")");
+        }
+        if (slots_out) slots_out->push_back((long long)table[(size_t)r * table_ld + p / dap::kPage] * dap::kPage + p % dap::kPage);
+    }
+    return DAP_OK;
+}
+
+int check_handle(const dap_handle* h) {
+    if (!h) return fail(DAP_INVALID_ARG, "null handle");
+    return DAP_OK;
+}
+
+int check_table_args(const int32_t* table, int32_t table_ld, int32_t n_table_rows, int32_t n_pages) {
+    DAP_REQUIRE(table && aligned4(table), DAP_INVALID_ARG, "table must be a non-null, 4-byte aligned device pointer");
+    DAP_REQUIRE(table_ld > 0 && n_table_rows > 0, DAP_INVALID_ARG, "table_ld and n_table_rows must be positive");
+    DAP_REQUIRE(n_pages > 0, DAP_INVALID_ARG, "n_pages must be positive");
+    return DAP_OK;
+}
+
+int check_stride(int64_t ld, int64_t width, const char* name) {
+    if (ld < width || ld % 8 != 0)
+        return fail(DAP_INVALID_ARG, std::string(name) + " must be >= the row width and a multiple of 8 elements");
+    return DAP_OK;
+}
+
+dap::AttnArgs attn_args(dap_handle* h, const uint16_t* q, int64_t ld_q, int32_t n, const int32_t* positions,
+                        const int32_t* rows, const int32_t* table, int32_t table_ld, int32_t n_table_rows,
+                        const uint16_t* k_pool, const uint16_t* v_pool, int32_t n_pages, uint16_t* out,
+                        int64_t ld_out) {
+    dap::AttnArgs a;
+    a.q = q; a.ld_q = ld_q; a.n_tokens = n; a.positions = positions; a.rows = rows;
+    a.table = table; a.table_ld = table_ld; a.n_table_rows = n_table_rows;
+    a.k_pool = k_pool; a.v_pool = v_pool; a.n_pages = n_pages; a.out = out; a.ld_out = ld_out;
+    a.n_q_heads = h->m.n_q_heads; a.n_kv_heads = h->m.n_kv_heads; a.head_dim = h->m.head_dim;
+    a.window = h->m.window; a.max_position = h->m.max_position; a.err = h->d_err;
+    return a;
+}
+
+// ---------------------------------------------------------------- entry bodies
+int do_write(dap_handle* h, const uint16_t* q, const uint16_t* k, const uint16_t* v, int64_t ld_in,
+             int32_t n_tokens, const int32_t* positions, const int32_t* rows, const int32_t* slots,
+             const int32_t* table, int32_t table_ld, int32_t n_table_rows, const uint16_t* q_gain,
+             const uint16_t* k_gain, uint16_t* q_out, int64_t ld_q_out, uint16_t* k_pool, uint16_t* v_pool,
+             int32_t n_pages, hipStream_t s) {
+    const dap_model& m = h->m;
+    const int64_t D = m.head_dim;
+    DAP_REQUIRE(n_tokens >= 0, DAP_INVALID_ARG, "n_tokens must be >= 0");
+    if (n_tokens == 0) return DAP_OK;
+    DAP_REQUIRE(q && k && v && q_out && k_pool && v_pool, DAP_INVALID_ARG, "null tensor pointer");
+    DAP_REQUIRE(aligned16(q) && aligned16(k) && aligned16(v) && aligned16(q_out) && aligned16(k_pool) && aligned16(v_pool),
+                DAP_INVALID_ARG, "bf16 tensors must be 16-byte aligned");
+    DAP_REQUIRE(positions && aligned4(positions), DAP_INVALID_ARG, "positions must be a non-null aligned pointer");
+    DAP_REQUIRE(slots || rows, DAP_INVALID_ARG, "either slots or rows (with the table) is required");
+    DAP_REQUIRE(n_pages > 0, DAP_INVALID_ARG, "n_pages must be positive");
+    if (!slots) {
+        int rc = check_table_args(table, table_ld, n_table_rows, n_pages);
+        if (rc) return rc;
+    }
+    if (int rc = check_stride(ld_in, std::max<int64_t>(m.n_q_heads, m.n_kv_heads) * D, "ld_in")) return rc;
+    if (int rc = check_stride(ld_q_out, m.n_q_heads * D, "ld_q_out")) return rc;
+    if (m.qk_norm) {
+        DAP_REQUIRE(q_gain && k_gain && aligned16(q_gain) && aligned16(k_gain), DAP_INVALID_ARG,
+                    "qk_norm needs 16-byte aligned q_gain and k_gain");
+    }
+    if (q_out == q) DAP_REQUIRE(ld_q_out == ld_in, DAP_INVALID_ARG, "in-place q_out needs ld_q_out == ld_in");
+
+    if (h->validate) {
+        std::vector<int32_t> hp, hr, hs, ht;
+        if (!to_host(hp, positions, n_tokens, s)) return fail(DAP_HIP_ERROR, "copying positions");
+        std::vector<long long> sl;
+        if (slots) {
+            if (!to_host(hs, slots, n_tokens, s)) return fail(DAP_HIP_ERROR, "copying slots");
+            for (int t = 0; t < n_tokens; ++t) {
+                if (hp[t] < 0 || hp[t] >= m.max_position) return fail(DAP_BAD_INDEX, "position out of range at " + std::to_string(t));
+                if (hs[t] < 0 || (long long)hs[t] >= (long long)n_pages * dap::kPage) return fail(DAP_BAD_INDEX, "slot out of range at " + std::to_string(t));
+                sl.push_back(hs[t]);
+            }
+        } else {
+            if (!to_host(hr, rows, n_tokens, s) || !to_host(ht, table, (size_t)table_ld * n_table_rows, s))
+                return fail(DAP_HIP_ERROR, "copying rows/table");
+            if (int rc = check_rows(h, hp, hr, ht, table_ld, n_table_rows, n_pages, false, &sl)) return rc;
+        }
+        std::unordered_set<long long> seen;
+        for (long long x : sl)
+            if (!seen.insert(x).second) return fail(DAP_BAD_INDEX, "two tokens write the same slot " + std::to_string(x));
+        if (int rc = begin_validate(h, s)) return rc;
+    }
+    dap::WriteArgs a;
+    a.q = q; a.k = k; a.v = v; a.ld_in = ld_in; a.n_tokens = n_tokens; a.positions = positions;
+    a.rows = rows; a.slots = slots; a.table = table; a.table_ld = table_ld; a.n_table_rows = n_table_rows;
+    a.q_gain = q_gain; a.k_gain = k_gain; a.q_out = q_out; a.ld_q_out = ld_q_out;
+    a.k_pool = k_pool; a.v_pool = v_pool; a.n_pages = n_pages;
+    a.n_q_heads = m.n_q_heads; a.n_kv_heads = m.n_kv_heads; a.head_dim = m.head_dim; a.max_position = m.max_position;
+    a.qk_norm = m.qk_norm; a.eps = m.qk_norm_eps; a.inv_freq = h->d_inv_freq; a.err = h->d_err;
+    hipError_t e = dap::launch_write(a, s, h->profiler());
+    if (e != hipSuccess) return hip_fail(e, "rope/write launch");
+    return h->validate ? end_validate(h, s) : DAP_OK;
+}
+
+int attn_common_checks(dap_handle* h, const uint16_t* q, int64_t ld_q, const int32_t* positions, const int32_t* table,
+                       int32_t table_ld, int32_t n_table_rows, const uint16_t* k_pool, const uint16_t* v_pool,
+                       int32_t n_pages, const uint16_t* out, int64_t ld_out) {
+    const int64_t W = (int64_t)h->m.n_q_heads * h->m.head_dim;
+    DAP_REQUIRE(q && out && k_pool && v_pool, DAP_INVALID_ARG, "null tensor pointer");
+    DAP_REQUIRE(aligned16(q) && aligned16(out) && aligned16(k_pool) && aligned16(v_pool), DAP_INVALID_ARG,
+                "bf16 tensors must be 16-byte aligned");
+    DAP_REQUIRE(positions && aligned4(positions), DAP_INVALID_ARG, "positions must be a non-null aligned pointer");
+    if (int rc = check_table_args(table, table_ld, n_table_rows, n_pages)) return rc;
+    if (int rc = check_stride(ld_q, W, "ld_q")) return rc;
+    if (int rc = check_stride(ld_out, W, "ld_out")) return rc;
+    DAP_REQUIRE(out != q, DAP_INVALID_ARG, "out must not alias q");
+    return DAP_OK;
+}
+
+int do_prefill(dap_handle* h, const uint16_t* q, int64_t ld_q, int32_t n_tokens, const int32_t* positions,
+               const int32_t* segments, int32_t n_segments, const int32_t* table, int32_t table_ld,
+               int32_t n_table_rows, const uint16_t* k_pool, const uint16_t* v_pool, int32_t n_pages, uint16_t* out,
+               int64_t ld_out, void* workspace, size_t workspace_bytes, hipStream_t s) {
+    DAP_REQUIRE(n_tokens >= 0, DAP_INVALID_ARG, "n_tokens must be >= 0");
+    if (n_tokens == 0) return DAP_OK;
+    DAP_REQUIRE(h->group == 1 || h->group == 2 || h->group == 4, DAP_UNSUPPORTED,
+                "prefill supports Hq/Hkv of 1, 2 or 4");
+    if (int rc = attn_common_checks(h, q, ld_q, positions, table, table_ld, n_table_rows, k_pool, v_pool, n_pages, out, ld_out))
+        return rc;
+    DAP_REQUIRE(segments && aligned4(segments), DAP_INVALID_ARG, "segments must be a non-null aligned pointer");
+    DAP_REQUIRE(n_segments > 0, DAP_INVALID_ARG, "n_segments must be positive");
+    const size_t need = dap::prefill_workspace(n_tokens, n_segments, h->group);
+    DAP_REQUIRE(workspace && workspace_bytes >= need && aligned16(workspace), DAP_WORKSPACE_TOO_SMALL,
+                "workspace must be 16-byte aligned and at least dap_prefill_workspace_bytes()");
+    const long long blocks = (long long)((need / sizeof(int)) - 2) * h->m.n_kv_heads;
+    DAP_REQUIRE(blocks < (1ll << 31), DAP_UNSUPPORTED, "too many prefill tiles for one launch");
+    if (h->validate) {
+        std::vector<int32_t> hp, hs, ht;
+        if (!to_host(hp, positions, n_tokens, s) || !to_host(hs, segments, n_tokens, s) ||
+            !to_host(ht, table, (size_t)table_ld * n_table_rows, s))
+            return fail(DAP_HIP_ERROR, "copying index arrays");
+        if (int rc = check_rows(h, hp, hs, ht, table_ld, n_table_rows, n_pages, true, nullptr)) return rc;
+        int runs = 0;
+        for (int t = 0; t < n_tokens; ++t) runs += (t == 0 || hs[t] != hs[t - 1]);
+        if (runs > n_segments) return fail(DAP_BAD_INDEX, "more runs of equal segment ids than n_segments");
+        if (int rc = begin_validate(h, s)) return rc;
+    }
+    dap::AttnArgs a = attn_args(h, q, ld_q, n_tokens, positions, segments, table, table_ld, n_table_rows, k_pool,
+                                v_pool, n_pages, out, ld_out);
+    hipError_t e = dap::launch_prefill(a, n_segments, workspace, s, h->profiler());
+    if (e != hipSuccess) return hip_fail(e, "prefill launch");
+    return h->validate ? end_validate(h, s) : DAP_OK;
+}
+
+int do_decode(dap_handle* h, const uint16_t* q, int64_t ld_q, int32_t n_rows, const int32_t* positions,
+              const int32_t* rows, const int32_t* table, int32_t table_ld, int32_t n_table_rows,
+              const uint16_t* k_pool, const uint16_t* v_pool, int32_t n_pages, uint16_t* out, int64_t ld_out,
+              void* workspace, size_t workspace_bytes, hipStream_t s) {
+    DAP_REQUIRE(n_rows >= 0, DAP_INVALID_ARG, "n_rows must be >= 0");
+    if (n_rows == 0) return DAP_OK;
+    DAP_REQUIRE(n_rows <= dap::kMaxDecodeRows, DAP_UNSUPPORTED, "at most 65535 rows per decode call");
+    if (int rc = attn_common_checks(h, q, ld_q, positions, table, table_ld, n_table_rows, k_pool, v_pool, n_pages, out, ld_out))
+        return rc;
+    DAP_REQUIRE(!rows || aligned4(rows), DAP_INVALID_ARG, "rows must be aligned");
+    const dap::DecodePlan plan = dap::decode_plan(n_rows, h->m.n_q_heads, h->m.n_kv_heads, h->m.head_dim,
+                                                  h->m.window, h->m.max_position);
+    DAP_REQUIRE(workspace && workspace_bytes >= plan.workspace_bytes && aligned16(workspace), DAP_WORKSPACE_TOO_SMALL,
+                "workspace must be 16-byte aligned and at least dap_decode_workspace_bytes()");
+    if (h->validate) {
+        std::vector<int32_t> hp, hr, ht;
+        if (!to_host(hp, positions, n_rows, s) || (rows && !to_host(hr, rows, n_rows, s)) ||
+            !to_host(ht, table, (size_t)table_ld * n_table_rows, s))
+            return fail(DAP_HIP_ERROR, "copying index arrays");
+        if (int rc = check_rows(h, hp, hr, ht, table_ld, n_table_rows, n_pages, true, nullptr)) return rc;
+        if (int rc = begin_validate(h, s)) return rc;
+    }
+    dap::AttnArgs a = attn_args(h, q, ld_q, n_rows, positions, rows, table, table_ld, n_table_rows, k_pool, v_pool,
+                                n_pages, out, ld_out);
+    hipError_t e = dap::launch_decode(a, plan, workspace, s, h->profiler());
+    if (e != hipSuccess) return hip_fail(e, "decode launch");
+    return h->validate ? end_validate(h, s) : DAP_OK;
+}
+
+size_t align256(size_t x) { return (x + 255) & ~size_t(255); }
+
+}  // namespace
+
+extern "C" {
+
+const char* dap_last_error(void) { return g_last_error.c_str(); }
+
+int dap_create(const dap_model* mp, dap_handle** out) {
+    DAP_REQUIRE(mp && out, DAP_INVALID_ARG, "null argument");
+    *out = nullptr;
+    const dap_model& m = *mp;
+    DAP_REQUIRE(m.n_q_heads > 0 && m.n_kv_heads > 0 && m.n_q_heads % m.n_kv_heads == 0, DAP_INVALID_ARG,
+                "need Hq > 0, Hkv > 0 and Hq % Hkv == 0");
+    DAP_REQUIRE(m.n_q_heads / m.n_kv_heads <= 16, DAP_UNSUPPORTED, "Hq / Hkv must be at most 16");
+    DAP_REQUIRE(m.head_dim == 64 || m.head_dim == 96 || m.head_dim == 128, DAP_UNSUPPORTED,
+                "head_dim must be 64, 96 or 128");
+    DAP_REQUIRE(m.page_size == dap::kPage, DAP_UNSUPPORTED, "page_size must be 64");
+    DAP_REQUIRE(m.window >= 0, DAP_INVALID_ARG, "window must be >= 0 (0 = none)");
+    DAP_REQUIRE(m.max_position > 0, DAP_INVALID_ARG, "max_position must be positive");
+    DAP_REQUIRE(m.rope_theta > 0 && std::isfinite(m.rope_theta), DAP_INVALID_ARG, "rope_theta must be positive");
+    if (m.llama3) {
+        DAP_REQUIRE(m.llama3_factor > 0 && m.llama3_low_freq_factor > 0 &&
+                        m.llama3_high_freq_factor > m.llama3_low_freq_factor && m.llama3_original_max_position > 0,
+                    DAP_INVALID_ARG, "llama3 needs factor > 0, high_freq_factor > low_freq_factor > 0, original > 0");
+    }
+    if (m.qk_norm) DAP_REQUIRE(m.qk_norm_eps > 0, DAP_INVALID_ARG, "qk_norm_eps must be positive");
+
+    dap_handle* h = new (std::nothrow) dap_handle();
+    if (!h) return fail(DAP_INVALID_ARG, "out of host memory");
+    h->m = m;
+    h->group = m.n_q_heads / m.n_kv_heads;
+    h->validate = 0;
+    h->d_inv_freq = nullptr;
+    h->d_err = nullptr;
+    h->prof_state = nullptr;
+    h->prof.st = nullptr;
+    h->h_inv_freq = build_inv_freq(m);
+    hipError_t e = hipGetDevice(&h->device);
+    if (e == hipSuccess) e = hipMalloc(&h->d_inv_freq, h->h_inv_freq.size() * sizeof(double));
+    if (e == hipSuccess) e = hipMalloc(&h->d_err, 256);
+    if (e == hipSuccess)
+        e = hipMemcpy(h->d_inv_freq, h->h_inv_freq.data(), h->h_inv_freq.size() * sizeof(double), hipMemcpyHostToDevice);
+    if (e == hipSuccess) e = hipMemset(h->d_err, 0, 256);
+    if (e != hipSuccess) {
+        dap_destroy(h);
+        return hip_fail(e, "dap_create");
+    }
+    *out = h;
+    return DAP_OK;
+}
+
+void dap_destroy(dap_handle* h) {
+    if (!h) return;
+    delete h->prof_state;
+    if (h->d_inv_freq) (void)hipFree(h->d_inv_freq);
+    if (h->d_err) (void)hipFree(h->d_err);
+    delete h;
+}
+
+int dap_set_validate(dap_handle* h, int on) {
+    if (int rc = check_handle(h)) return rc;
+    h->validate = on ? 1 : 0;
+    return DAP_OK;
+}
+
+int dap_set_profiling(dap_handle* h, int on) {
+    if (int rc = check_handle(h)) return rc;
+    if (on && !h->prof_state) {
+        auto* st = new (std::nothrow) dap::ProfilerState();
+        if (!st) return fail(DAP_INVALID_ARG, "out of host memory");
+        hipError_t e = st->init();
+        if (e != hipSuccess) {
+            delete st;
+            return hip_fail(e, "creating timing events");
+        }
+        h->prof_state = st;
+        h->prof.st = st;
+    } else if (!on && h->prof_state) {
+        while (h->prof_state->count > 0)
+            if (h->prof_state->drain_one() != hipSuccess) break;
+        delete h->prof_state;
+        h->prof_state = nullptr;
+        h->prof.st = nullptr;
+    }
+    return DAP_OK;
+}
+
+int dap_profile_read(dap_handle* h, double* total_ms, int64_t* launches, int reset) {
+    if (int rc = check_handle(h)) return rc;
+    DAP_REQUIRE(h->prof_state, DAP_INVALID_ARG, "profiling is off");
+    dap::ProfilerState* st = h->prof_state;
+    while (st->count > 0) {
+        hipError_t e = st->drain_one();
+        if (e != hipSuccess) return hip_fail(e, "reading timing events");
+    }
+    for (int k = 0; k < DAP_N_KERNELS; ++k) {
+        if (total_ms) total_ms[k] = st->total_ms[k];
+        if (launches) launches[k] = st->launches[k];
+        if (reset) {
+            st->total_ms[k] = 0.0;
+            st->launches[k] = 0;
+        }
+    }
+    return DAP_OK;
+}
+
+int dap_inv_freq(const dap_handle* h, double* out, int32_t n) {
+    if (int rc = check_handle(h)) return rc;
+    DAP_REQUIRE(out && n == (int32_t)h->h_inv_freq.size(), DAP_INVALID_ARG, "n must equal head_dim / 2");
+    std::memcpy(out, h->h_inv_freq.data(), n * sizeof(double));
+    return DAP_OK;
+}
+
+int dap_rope_qknorm_write_pages(dap_handle* h, const uint16_t* q, const uint16_t* k, const uint16_t* v, int64_t ld_in,
+                                int32_t n_tokens, const int32_t* positions, const int32_t* rows, const int32_t* slots,
+                                const int32_t* table, int32_t table_ld, int32_t n_table_rows, const uint16_t* q_gain,
+                                const uint16_t* k_gain, uint16_t* q_out, int64_t ld_q_out, uint16_t* k_pool,
+                                uint16_t* v_pool, int32_t n_pages, void* stream) {
+    if (int rc = check_handle(h)) return rc;
+    return do_write(h, q, k, v, ld_in, n_tokens, positions, rows, slots, table, table_ld, n_table_rows, q_gain, k_gain,
+                    q_out, ld_q_out, k_pool, v_pool, n_pages, static_cast<hipStream_t>(stream));
+}
+
+size_t dap_prefill_workspace_bytes(const dap_handle* h, int32_t n_tokens, int32_t n_segments) {
+    if (!h || n_tokens < 0 || n_segments < 0) return 0;
+    return dap::prefill_workspace(n_tokens, std::max(n_segments, 1), h->group);
+}
+
+int dap_attn_prefill_packed(dap_handle* h, const uint16_t* q, int64_t ld_q, int32_t n_tokens, const int32_t* positions,
+                            const int32_t* segments, int32_t n_segments, const int32_t* table, int32_t table_ld,
+                            int32_t n_table_rows, const uint16_t* k_pool, const uint16_t* v_pool, int32_t n_pages,
+                            uint16_t* out, int64_t ld_out, void* workspace, size_t workspace_bytes, void* stream) {
+    if (int rc = check_handle(h)) return rc;
+    return do_prefill(h, q, ld_q, n_tokens, positions, segments, n_segments, table, table_ld, n_table_rows, k_pool,
+                      v_pool, n_pages, out, ld_out, workspace, workspace_bytes, static_cast<hipStream_t>(stream));
+}
+
+size_t dap_decode_workspace_bytes(const dap_handle* h, int32_t n_rows) {
+    if (!h || n_rows < 0) return 0;
+    return dap::decode_plan(n_rows, h->m.n_q_heads, h->m.n_kv_heads, h->m.head_dim, h->m.window, h->m.max_position)
+        .workspace_bytes;
+}
+
+int dap_attn_decode_paged(dap_handle* h, const uint16_t* q, int64_t ld_q, int32_t n_rows, const int32_t* positions,
+                          const int32_t* rows, const int32_t* table, int32_t table_ld, int32_t n_table_rows,
+                          const uint16_t* k_pool, const uint16_t* v_pool, int32_t n_pages, uint16_t* out,
+                          int64_t ld_out, void* workspace, size_t workspace_bytes, void* stream) {
+    if (int rc = check_handle(h)) return rc;
+    return do_decode(h, q, ld_q, n_rows, positions, rows, table, table_ld, n_table_rows, k_pool, v_pool, n_pages, out,
+                     ld_out, workspace, workspace_bytes, static_cast<hipStream_t>(stream));
+}
+
+// Step workspace: the decode workspace first (its counters persist between
+// calls at a fixed place), then the prefill's tile list (rewritten every call).
+size_t dap_step_workspace_bytes(const dap_handle* h, int32_t n_prompt, int32_t n_segments, int32_t n_step) {
+    if (!h || n_prompt < 0 || n_step < 0) return 0;
+    return align256(dap_decode_workspace_bytes(h, n_step)) + dap_prefill_workspace_bytes(h, n_prompt, n_segments);
+}
+
+int dap_step_paged(dap_handle* h, const uint16_t* q, const uint16_t* k, const uint16_t* v, int64_t ld_in,
+                   int32_t n_prompt, int32_t n_segments, int32_t n_step, const int32_t* positions, const int32_t* rows,
+                   const int32_t* slots, const int32_t* table, int32_t table_ld, int32_t n_table_rows,
+                   const uint16_t* q_gain, const uint16_t* k_gain, uint16_t* q_out, int64_t ld_q_out,
+                   uint16_t* k_pool, uint16_t* v_pool, int32_t n_pages, uint16_t* out, int64_t ld_out,
+                   void* workspace, size_t workspace_bytes, void* stream) {
+    if (int rc = check_handle(h)) return rc;
+    DAP_REQUIRE(n_prompt >= 0 && n_step >= 0, DAP_INVALID_ARG, "counts must be >= 0");
+    DAP_REQUIRE(rows && aligned4(rows), DAP_INVALID_ARG, "step_paged needs rows");
+    const size_t need = dap_step_workspace_bytes(h, n_prompt, n_segments, n_step);
+    DAP_REQUIRE(workspace && workspace_bytes >= need && aligned16(workspace), DAP_WORKSPACE_TOO_SMALL,
+                "workspace must be 16-byte aligned and at least dap_step_workspace_bytes()");
+    hipStream_t s = static_cast<hipStream_t>(stream);
+    const int n_all = n_prompt + n_step;
+    int rc = do_write(h, q, k, v, ld_in, n_all, positions, rows, slots, table, table_ld, n_table_rows, q_gain, k_gain,
+                      q_out, ld_q_out, k_pool, v_pool, n_pages, s);
+    if (rc) return rc;
+    const size_t dec_bytes = align256(dap_decode_workspace_bytes(h, n_step));
+    if (n_prompt > 0) {
+        rc = do_prefill(h, q_out, ld_q_out, n_prompt, positions, rows, n_segments, table, table_ld, n_table_rows,
+                        k_pool, v_pool, n_pages, out, ld_out, static_cast<char*>(workspace) + dec_bytes,
+                        workspace_bytes - dec_bytes, s);
+        if (rc) return rc;
+    }
+    if (n_step > 0) {
+        rc = do_decode(h, q_out + (int64_t)n_prompt * ld_q_out, ld_q_out, n_step, positions + n_prompt,
+                       rows + n_prompt, table, table_ld, n_table_rows, k_pool, v_pool, n_pages,
+                       out + (int64_t)n_prompt * ld_out, ld_out, workspace, dec_bytes, s);
+        if (rc) return rc;
+    }
+    return DAP_OK;
+}
+
+}  // extern "C"

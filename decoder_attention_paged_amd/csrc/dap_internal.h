@@ -1,0 +1,151 @@
+// Internal declarations shared by the library's HIP translation units.
+// Device helpers (bf16 conversions, MFMA vector types) and the launchers
+// each kernel file exports to the C-ABI layer.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+#include "../../include/dap.h"
+
+namespace dap {
+
+constexpr int kPage = 64;
+
+// Bits of the device error word (kernels OR them in when an index read from
+// device memory is out of range; the entry is skipped).
+enum ErrorBits : unsigned {
+    kErrPosition = 1u,
+    kErrRow = 2u,
+    kErrPage = 4u,
+    kErrSlot = 8u,
+    kErrTable = 16u,
+};
+
+typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
+typedef float f32x4 __attribute__((ext_vector_type(4)));
+typedef float f32x16 __attribute__((ext_vector_type(16)));
+typedef unsigned u32x4 __attribute__((ext_vector_type(4)));
+
+__device__ __forceinline__ float bf16_to_f32(uint32_t b) { return __uint_as_float(b << 16); }
+
+// float32 -> bf16, round to nearest even; NaN stays a quiet NaN.
+__device__ __forceinline__ uint32_t f32_to_bf16(float x) {
+    uint32_t u = __float_as_uint(x);
+    if ((u & 0x7fffffffu) > 0x7f800000u) return ((u >> 16) | 0x40u) & 0xffffu;
+    u += 0x7fffu + ((u >> 16) & 1u);
+    return u >> 16;
+}
+
+// float64 -> bf16 in one rounding, to nearest even, from the bit pattern.
+// Normal bf16 range keeps 7 stored mantissa bits of the 52; below 2^-126 the
+// grid is the subnormal quantum 2^-133; a carry out of the largest finite
+// value gives infinity.
+__device__ __forceinline__ uint32_t f64_to_bf16(double x) {
+    const uint64_t b = (uint64_t)__double_as_longlong(x);
+    const uint32_t sign = (uint32_t)(b >> 48) & 0x8000u;
+    const uint64_t a = b & 0x7fffffffffffffffull;
+    if (a > 0x7ff0000000000000ull) return sign | 0x7fc0u;           // NaN
+    const int e = (int)(a >> 52) - 1023;                             // unbiased exponent
+    if (e > 127) return sign | 0x7f80u;                              // inf or too large
+    const uint64_t mant = a & 0x000fffffffffffffull;
+    if (e >= -126) {
+        const uint32_t kept = (uint32_t)(mant >> 45);
+        const uint64_t rem = mant & ((1ull << 45) - 1);
+        const uint64_t half = 1ull << 44;
+        uint32_t r = ((uint32_t)(e + 127) << 7) | kept;
+        if (rem > half || (rem == half && (kept & 1u))) r += 1;     // may carry into exponent
+        return sign | r;
+    }
+    if ((a >> 52) == 0) return sign;                                 // fp64 zero/subnormal
+    // bf16 subnormal: value = full * 2^(e-52); quantum 2^-133
+    const uint64_t full = mant | (1ull << 52);
+    const int shift = 45 + (-126 - e);                               // >= 46
+    if (shift >= 64) return sign;
+    const uint64_t kept = full >> shift;
+    const uint64_t rem = full & ((1ull << shift) - 1);
+    const uint64_t half = 1ull << (shift - 1);
+    uint64_t r = kept;
+    if (rem > half || (rem == half && (kept & 1u))) r += 1;
+    return sign | (uint32_t)r;
+}
+
+// ---------------------------------------------------------------------------
+// Kernel timing hook: when a handle has profiling on, every launch is
+// bracketed by begin/end, which record a pair of hipEvents on the launch
+// stream (see dap_set_profiling).
+struct ProfilerState;
+struct Profiler {
+    ProfilerState* st;
+    void begin(int kind, hipStream_t s);
+    void end(int kind, hipStream_t s);
+};
+
+// Launchers (host functions living next to their kernels).
+
+struct WriteArgs {
+    const uint16_t* q;
+    const uint16_t* k;
+    const uint16_t* v;
+    int64_t ld_in;
+    int32_t n_tokens;
+    const int32_t* positions;
+    const int32_t* rows;
+    const int32_t* slots;
+    const int32_t* table;
+    int32_t table_ld;
+    int32_t n_table_rows;
+    const uint16_t* q_gain;
+    const uint16_t* k_gain;
+    uint16_t* q_out;
+    int64_t ld_q_out;
+    uint16_t* k_pool;
+    uint16_t* v_pool;
+    int32_t n_pages;
+    int32_t n_q_heads, n_kv_heads, head_dim, max_position;
+    int32_t qk_norm;
+    double eps;
+    const double* inv_freq;   // device [D/2]
+    unsigned* err;
+};
+hipError_t launch_write(const WriteArgs& a, hipStream_t s, Profiler* prof);
+
+struct AttnArgs {
+    const uint16_t* q;
+    int64_t ld_q;
+    int32_t n_tokens;          // prefill: tokens; decode: rows
+    const int32_t* positions;
+    const int32_t* rows;       // prefill: segments (table rows); decode: nullable
+    const int32_t* table;
+    int32_t table_ld;
+    int32_t n_table_rows;
+    const uint16_t* k_pool;
+    const uint16_t* v_pool;
+    int32_t n_pages;
+    uint16_t* out;
+    int64_t ld_out;
+    int32_t n_q_heads, n_kv_heads, head_dim, window, max_position;
+    unsigned* err;
+};
+
+// Decode: split count and workspace layout.
+// Workspace: [counters: kMaxDecodeRows * Hkv ints, padded to 256 B]
+//            [partials: n_rows * Hq * max_splits * (D + 2) floats]
+// The counters must be zero before the first call; every call leaves them zero.
+constexpr int kMaxDecodeRows = 65535;
+struct DecodePlan {
+    int pages_per_split;
+    int max_splits;
+    size_t counter_bytes;
+    size_t workspace_bytes;
+};
+DecodePlan decode_plan(int n_rows, int n_q_heads, int n_kv_heads, int head_dim, int window,
+                       int max_position);
+hipError_t launch_decode(const AttnArgs& a, const DecodePlan& plan, void* workspace, hipStream_t s,
+                         Profiler* prof);
+
+// Prefill: tile list sizing and launch.
+size_t prefill_workspace(int n_tokens, int n_segments, int group);
+hipError_t launch_prefill(const AttnArgs& a, int n_segments, void* workspace, hipStream_t s, Profiler* prof);
+
+}  // namespace dap

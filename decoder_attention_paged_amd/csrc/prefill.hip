@@ -1,0 +1,367 @@
+// Packed prefill over pages: flash-style MFMA attention.
+//
+// Sources: "Phi-3 Mini 4K Instruct" files, src/attention.linnet
+// (prefill_packed: token i sees token j iff they share a segment and
+// positions[j] <= positions[i] and positions[j] > positions[i] - WINDOW;
+// scores scaled by rsqrt(head_dim)); "Mistral 7B Instruct v0.3", Entries
+// (prefill_paged: each token attends over its row's pages up to its
+// position, which covers chunks and shared prefixes).
+//
+// A tile-list pass cuts the packed tokens into runs of equal segment id and
+// each run into tiles of at most 128/g tokens. One workgroup (4 waves) takes
+// one (tile, kv head): wave w owns 32 query rows = one of the g query heads
+// sharing the kv head, for 32 of the tile's tokens, so each K/V page tile is
+// read from memory once per workgroup for all g heads. Per 64-key page the
+// workgroup stages K (slot-major) and V^T (dim-major) through LDS, and each
+// wave computes S^T = K Q^T and O^T += V^T P^T with 32x32x16 bf16 MFMAs and
+// an online softmax in float32 (exp2 with the scale folded in). Pages fully
+// outside a wave's rows are skipped; only pages that straddle a row's causal
+// or window edge are masked element by element. Workgroups are numbered
+// kv-head-fastest so blocks sharing a kv head land on the same XCD (L2).
+#include "dap_internal.h"
+
+namespace dap {
+
+namespace {
+
+constexpr int kPrefillThreads = 256;   // 4 waves
+constexpr int kTilesThreads = 1024;
+constexpr float kLog2e = 1.4426950408889634f;
+constexpr unsigned kErrSegments = 32u;
+
+__device__ __forceinline__ bf16x8 as_bf16x8(u32x4 u) { return __builtin_bit_cast(bf16x8, u); }
+
+// ---------------------------------------------------------------- tile list
+// tiles[k] = first token of tile k (k < n_tiles), tiles[n_tiles] = end of the
+// last tile, tiles[cap + 1] = n_tiles (at most cap tiles are kept).
+// A tile starts where (t - start of t's run) is a multiple of bm.
+__global__ __launch_bounds__(kTilesThreads) void prefill_tiles_kernel(const int32_t* __restrict__ seg, int n,
+                                                                      int bm, int cap, int* __restrict__ tiles,
+                                                                      unsigned* err) {
+    __shared__ int s_scan[kTilesThreads];
+    const int tid = threadIdx.x;
+    const int chunk = (n + kTilesThreads - 1) / kTilesThreads;
+    const int c0 = min(n, tid * chunk);
+    const int c1 = min(n, c0 + chunk);
+
+    // last run start inside my chunk (-1 if none)
+    int my_start = -1;
+    for (int t = c0; t < c1; ++t)
+        if (t == 0 || seg[t] != seg[t - 1]) my_start = t;
+    // exclusive max-scan of run starts
+    s_scan[tid] = my_start;
+    __syncthreads();
+    for (int off = 1; off < kTilesThreads; off <<= 1) {
+        const int v = tid >= off ? s_scan[tid - off] : -1;
+        __syncthreads();
+        s_scan[tid] = max(s_scan[tid], v);
+        __syncthreads();
+    }
+    int rs = tid > 0 ? s_scan[tid - 1] : -1;
+    __syncthreads();
+
+    // count tile starts in my chunk
+    int cnt = 0;
+    int r = rs;
+    for (int t = c0; t < c1; ++t) {
+        if (t == 0 || seg[t] != seg[t - 1]) r = t;
+        if ((t - r) % bm == 0) ++cnt;
+    }
+    // inclusive sum-scan of counts
+    s_scan[tid] = cnt;
+    __syncthreads();
+    for (int off = 1; off < kTilesThreads; off <<= 1) {
+        const int v = tid >= off ? s_scan[tid - off] : 0;
+        __syncthreads();
+        s_scan[tid] += v;
+        __syncthreads();
+    }
+    int idx = s_scan[tid] - cnt;
+    const int total = s_scan[kTilesThreads - 1];
+    r = rs;
+    for (int t = c0; t < c1; ++t) {
+        if (t == 0 || seg[t] != seg[t - 1]) r = t;
+        if ((t - r) % bm == 0) {
+            // index cap holds the first dropped tile's start (the end of the last kept one)
+            if (idx <= cap) tiles[idx] = t;
+            ++idx;
+        }
+    }
+    if (tid == 0) {
+        if (total <= cap) tiles[total] = n;
+        else atomicOr(err, kErrSegments);
+        tiles[cap + 1] = min(total, cap);
+    }
+}
+
+__device__ __forceinline__ int wave_min(int v) {
+#pragma unroll
+    for (int o = 32; o > 0; o >>= 1) v = min(v, __shfl_xor(v, o));
+    return v;
+}
+__device__ __forceinline__ int wave_max(int v) {
+#pragma unroll
+    for (int o = 32; o > 0; o >>= 1) v = max(v, __shfl_xor(v, o));
+    return v;
+}
+
+// Key (within a 32-key S block) held in A-row i: bits 2 and 3 of i swapped,
+// so that in the 32x32 output layout lane group g's registers 8h..8h+7 are
+// the 8 contiguous keys 16h + 8g .. 16h + 8g + 7 the PV step needs.
+__device__ __forceinline__ int swap23(int i) { return (i & ~12) | ((i & 4) << 1) | ((i & 8) >> 1); }
+
+template <int D, int G>
+__global__ __launch_bounds__(kPrefillThreads, 2) void prefill_kernel(AttnArgs a, const int* __restrict__ tiles,
+                                                                     int cap) {
+    constexpr int BM = 128 / G;         // tokens per tile
+    constexpr int KS = D + 8;           // LDS row stride of K (elements)
+    constexpr int VS = kPage + 8;       // LDS row stride of V^T (elements)
+    constexpr int kSteps = D / 16;      // QK k-steps
+    constexpr int kDimBlocks = D / 32;  // PV output blocks
+    constexpr int kChunks = D / 32;     // 16-byte chunks per thread per tensor per page
+
+    __shared__ __attribute__((aligned(16))) uint16_t s_k[kPage * KS];
+    __shared__ __attribute__((aligned(16))) uint16_t s_v[D * VS];
+
+    const int n_tiles = tiles[cap + 1];
+    const int kh = blockIdx.x % a.n_kv_heads;
+    const int tile = blockIdx.x / a.n_kv_heads;
+    if (tile >= n_tiles) return;
+    const int t0 = tiles[tile];
+    const int t1 = min(tiles[tile + 1], t0 + BM);
+
+    const int tid = threadIdx.x;
+    const int wave = tid >> 6;
+    const int lane = tid & 63;
+    const int row = lane & 31;
+    const int half = lane >> 5;
+    const int hq = kh * G + (wave % G);
+    const int tok = t0 + 32 * (wave / G) + row;
+    const bool row_valid = tok < t1;
+
+    // table row of the tile (all its tokens share the segment)
+    const int trow = a.rows[t0];
+    if (trow < 0 || trow >= a.n_table_rows) {
+        if (tid == 0 && kh == 0) atomicOr(a.err, kErrRow);
+        return;
+    }
+
+    // per-row attended range [lo, p]
+    int p = -1, lo = 1 << 30;
+    if (row_valid) {
+        p = a.positions[tok];
+        if (p < 0 || p >= a.max_position) {
+            if (kh == 0) atomicOr(a.err, kErrPosition);
+            p = -1;
+        } else {
+            lo = a.window > 0 ? max(0, p - a.window + 1) : 0;
+        }
+    }
+    // workgroup-wide key range over every token of the tile
+    int kmin = 1 << 30, kmax = -1;
+    for (int t = t0 + lane; t < t1; t += 64) {
+        const int pp = a.positions[t];
+        if (pp >= 0 && pp < a.max_position) {
+            kmax = max(kmax, pp);
+            kmin = min(kmin, a.window > 0 ? max(0, pp - a.window + 1) : 0);
+        }
+    }
+    kmin = wave_min(kmin);
+    kmax = wave_max(kmax);
+    if (kmax < 0) return;                        // uniform: no valid token
+    if ((kmax >> 6) >= a.table_ld) {
+        if (tid == 0 && kh == 0) atomicOr(a.err, kErrTable);
+        return;
+    }
+    // this wave's rows
+    const int w_pmax = wave_max(p);
+    const int w_lomin = wave_min(lo);
+    const int w_pmin = wave_min(row_valid && p >= 0 ? p : (1 << 30));
+    const int w_lomax = wave_max(row_valid && p >= 0 ? lo : -1);
+
+    // Q^T as the B operand: column = query row, k-group = dims 16s + 8*half
+    bf16x8 qf[kSteps];
+    {
+        const uint16_t* qr = a.q + (long long)(row_valid ? tok : t0) * a.ld_q + (long long)hq * D + 8 * half;
+#pragma unroll
+        for (int s = 0; s < kSteps; ++s) {
+            u32x4 u = *reinterpret_cast<const u32x4*>(qr + 16 * s);
+            if (!row_valid || p < 0) u = u32x4{0u, 0u, 0u, 0u};
+            qf[s] = as_bf16x8(u);
+        }
+    }
+
+    const float c = kLog2e / sqrtf((float)D);
+    float m = -INFINITY;
+    float lsum = 0.f;
+    f32x16 o[kDimBlocks];
+#pragma unroll
+    for (int db = 0; db < kDimBlocks; ++db)
+#pragma unroll
+        for (int r = 0; r < 16; ++r) o[db][r] = 0.f;
+
+    const int* tr = a.table + (long long)trow * a.table_ld;
+    const int j_first = kmin >> 6;
+    const int j_last = kmax >> 6;
+
+    u32x4 pk[kChunks], pv[kChunks];
+    auto prefetch = [&](int j) -> bool {
+        const int pg = tr[j];
+        if (pg < 0 || pg >= a.n_pages) return false;
+        const uint16_t* kt = a.k_pool + ((long long)pg * a.n_kv_heads + kh) * (kPage * D);
+        const uint16_t* vt = a.v_pool + ((long long)pg * a.n_kv_heads + kh) * (kPage * D);
+#pragma unroll
+        for (int i = 0; i < kChunks; ++i) {
+            const int cidx = tid + kPrefillThreads * i;
+            pk[i] = *reinterpret_cast<const u32x4*>(kt + 8 * cidx);
+            pv[i] = *reinterpret_cast<const u32x4*>(vt + 8 * cidx);
+        }
+        return true;
+    };
+    bool have = prefetch(j_first);
+
+    for (int j = j_first; j <= j_last; ++j) {
+        __syncthreads();                       // everyone is done reading the previous tile
+        const bool cur = have;
+        if (cur) {
+#pragma unroll
+            for (int i = 0; i < kChunks; ++i) {
+                const int cidx = tid + kPrefillThreads * i;
+                const int kr = cidx / (D / 8), kc = cidx % (D / 8);
+                *reinterpret_cast<u32x4*>(&s_k[kr * KS + 8 * kc]) = pk[i];
+                const int vr = cidx / (kPage / 8), vc = cidx % (kPage / 8);
+                *reinterpret_cast<u32x4*>(&s_v[vr * VS + 8 * vc]) = pv[i];
+            }
+        } else if (tid == 0 && kh == 0) {
+            atomicOr(a.err, kErrPage);
+        }
+        __syncthreads();
+        if (j < j_last) have = prefetch(j + 1);
+        if (!cur) continue;
+
+        const int k0 = j * kPage;
+        if (k0 > w_pmax || k0 + kPage - 1 < w_lomin) continue;    // nothing visible to this wave
+
+        // S^T = K Q^T : two 32-key blocks
+        f32x16 sc[2];
+#pragma unroll
+        for (int blk = 0; blk < 2; ++blk) {
+            f32x16 acc;
+#pragma unroll
+            for (int r = 0; r < 16; ++r) acc[r] = 0.f;
+            const uint16_t* kr = &s_k[(32 * blk + swap23(row)) * KS + 8 * half];
+#pragma unroll
+            for (int s = 0; s < kSteps; ++s) {
+                const u32x4 kf = *reinterpret_cast<const u32x4*>(kr + 16 * s);
+                acc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(as_bf16x8(kf), qf[s], acc, 0, 0, 0);
+            }
+            sc[blk] = acc * c;
+        }
+        // mask where this page crosses an edge of some row's range
+        if (k0 < w_lomax || k0 + kPage - 1 > w_pmin) {
+#pragma unroll
+            for (int blk = 0; blk < 2; ++blk)
+#pragma unroll
+                for (int r = 0; r < 16; ++r) {
+                    const int q4 = r >> 2;
+                    const int kp = k0 + 32 * blk + 16 * (q4 >> 1) + 8 * half + 4 * (q4 & 1) + (r & 3);
+                    if (kp < lo || kp > p) sc[blk][r] = -INFINITY;
+                }
+        }
+        float mx = -INFINITY;
+#pragma unroll
+        for (int blk = 0; blk < 2; ++blk)
+#pragma unroll
+            for (int r = 0; r < 16; ++r) mx = fmaxf(mx, sc[blk][r]);
+        mx = fmaxf(mx, __shfl_xor(mx, 32));
+        const float m_new = fmaxf(m, mx);
+        const float m_ref = m_new == -INFINITY ? 0.f : m_new;
+        const float alpha = exp2f(m - m_ref);
+        float ps = 0.f;
+#pragma unroll
+        for (int blk = 0; blk < 2; ++blk)
+#pragma unroll
+            for (int r = 0; r < 16; ++r) {
+                const float e = exp2f(sc[blk][r] - m_ref);
+                sc[blk][r] = e;
+                ps += e;
+            }
+        lsum = lsum * alpha + ps;
+        m = m_new;
+#pragma unroll
+        for (int db = 0; db < kDimBlocks; ++db) o[db] *= alpha;
+
+        // O^T += V^T P^T : four 16-key steps
+#pragma unroll
+        for (int t = 0; t < 4; ++t) {
+            bf16x8 pf;
+#pragma unroll
+            for (int e = 0; e < 8; ++e) pf[e] = (__bf16)sc[t >> 1][8 * (t & 1) + e];
+#pragma unroll
+            for (int db = 0; db < kDimBlocks; ++db) {
+                const u32x4 vf = *reinterpret_cast<const u32x4*>(&s_v[(32 * db + row) * VS + 16 * t + 8 * half]);
+                o[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(as_bf16x8(vf), pf, o[db], 0, 0, 0);
+            }
+        }
+    }
+
+    lsum += __shfl_xor(lsum, 32);
+    if (!row_valid || p < 0) return;
+    const float inv = lsum > 0.f ? 1.f / lsum : 0.f;
+    uint16_t* dst = a.out + (long long)tok * a.ld_out + (long long)hq * D;
+#pragma unroll
+    for (int db = 0; db < kDimBlocks; ++db)
+#pragma unroll
+        for (int q4 = 0; q4 < 4; ++q4) {
+            uint32_t w0 = f32_to_bf16(o[db][4 * q4 + 0] * inv) | (f32_to_bf16(o[db][4 * q4 + 1] * inv) << 16);
+            uint32_t w1 = f32_to_bf16(o[db][4 * q4 + 2] * inv) | (f32_to_bf16(o[db][4 * q4 + 3] * inv) << 16);
+            *reinterpret_cast<uint2*>(dst + 32 * db + 8 * q4 + 4 * half) = make_uint2(w0, w1);
+        }
+}
+
+template <int D>
+hipError_t launch_prefill_d(const AttnArgs& a, int G, int cap, const int* tiles, hipStream_t s) {
+    dim3 grid((unsigned)cap * a.n_kv_heads), block(kPrefillThreads);
+    switch (G) {
+        case 1: hipLaunchKernelGGL((prefill_kernel<D, 1>), grid, block, 0, s, a, tiles, cap); break;
+        case 2: hipLaunchKernelGGL((prefill_kernel<D, 2>), grid, block, 0, s, a, tiles, cap); break;
+        case 4: hipLaunchKernelGGL((prefill_kernel<D, 4>), grid, block, 0, s, a, tiles, cap); break;
+        default: return hipErrorInvalidValue;
+    }
+    return hipGetLastError();
+}
+
+int tile_cap(int n_tokens, int n_segments, int group) {
+    const int bm = 128 / group;
+    return (n_tokens + bm - 1) / bm + n_segments;
+}
+
+}  // namespace
+
+size_t prefill_workspace(int n_tokens, int n_segments, int group) {
+    return (size_t)(tile_cap(n_tokens, n_segments, group) + 2) * sizeof(int);
+}
+
+hipError_t launch_prefill(const AttnArgs& a, int n_segments, void* workspace, hipStream_t s, Profiler* prof) {
+    if (a.n_tokens <= 0) return hipSuccess;
+    const int G = a.n_q_heads / a.n_kv_heads;
+    const int cap = tile_cap(a.n_tokens, n_segments, G);
+    int* tiles = static_cast<int*>(workspace);
+    if (prof) prof->begin(DAP_KERNEL_PREFILL_TILES, s);
+    hipLaunchKernelGGL(prefill_tiles_kernel, dim3(1), dim3(kTilesThreads), 0, s, a.rows, a.n_tokens, 128 / G, cap,
+                       tiles, a.err);
+    if (prof) prof->end(DAP_KERNEL_PREFILL_TILES, s);
+    hipError_t e = hipGetLastError();
+    if (e != hipSuccess) return e;
+    if (prof) prof->begin(DAP_KERNEL_PREFILL, s);
+    switch (a.head_dim) {
+        case 64: e = launch_prefill_d<64>(a, G, cap, tiles, s); break;
+        case 96: e = launch_prefill_d<96>(a, G, cap, tiles, s); break;
+        case 128: e = launch_prefill_d<128>(a, G, cap, tiles, s); break;
+        default: return hipErrorInvalidValue;
+    }
+    if (prof) prof->end(DAP_KERNEL_PREFILL, s);
+    return e;
+}
+
+}  // namespace dap

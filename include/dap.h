@@ -1,0 +1,241 @@
+/*
+ * dap.h -- paged decoder attention core for AMD MI355X (gfx950), C ABI.
+ *
+ * The attention core of a Llama / Phi-3 / Mistral / Qwen3 decoder layer:
+ * pre-rope Q/K/V in, optional per-head QK-RMSNorm, rotary positions
+ * (optional llama3 bands), K/V written into a pool of 64-position pages,
+ * then causal (optionally windowed) grouped-query attention over each row's
+ * pages, for packed prompts and for one decode token per row.
+ *
+ * Conventions for every call below
+ *  - Pointers named q, k, v, qkv, *_pool, out, table, positions, rows,
+ *    slots, segments, workspace, *_gain are DEVICE pointers; the model
+ *    struct, handle and output arguments of the query functions are host.
+ *  - bf16 tensors are passed as uint16_t bit patterns (IEEE bfloat16).
+ *  - Every call is asynchronous on `stream` (a hipStream_t; NULL = the
+ *    default stream) and ordered with other work on that stream. No call
+ *    after dap_create allocates, frees or synchronises, except in validate
+ *    mode (dap_set_validate), which adds host-side content checks (copies
+ *    of the index arrays and a stream synchronisation).
+ *  - The caller owns every buffer; the handle owns only its frequency
+ *    table and a small device error word.
+ *  - Return value: DAP_OK (0) or a negative status; dap_last_error()
+ *    returns a thread-local message for the last failure. Nothing aborts
+ *    and no C++ exception crosses this boundary.
+ *  - Kernels bounds-check every index they read from device memory (page
+ *    ids, rows, positions, slots); an out-of-range entry is skipped (its
+ *    output left unspecified, no memory outside the buffers touched) and
+ *    flagged in the handle's error word, which validate mode reports as
+ *    DAP_BAD_INDEX.
+ *
+ * Page pool layout (bf16), n_pages pages of 64 positions each:
+ *   K pool [n_pages][n_kv_heads][64][head_dim]   slot-major page tiles
+ *   V pool [n_pages][n_kv_heads][head_dim][64]   dim-major page tiles
+ * Position j of table row r lives in page table[r*table_ld + j/64] at index
+ * j%64; its slot number is page*64 + j%64. (The pages: "Mistral 7B Instruct
+ * v0.3", Entries table, decode_paged: a pool of positions in pages of
+ * PageSize 64, row b's positions in the pages table[b] lists.)
+ */
+#ifndef DAP_H
+#define DAP_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+enum {
+    DAP_OK = 0,
+    DAP_INVALID_ARG = -1,          /* bad pointer, count, stride or alignment */
+    DAP_UNSUPPORTED = -2,          /* head_dim not 64/96/128, page_size not 64, ... */
+    DAP_WORKSPACE_TOO_SMALL = -3,
+    DAP_HIP_ERROR = -4,            /* a HIP runtime call failed */
+    DAP_BAD_INDEX = -5             /* validate mode: an index array entry out of range */
+};
+
+/* Model constants, fixed for a handle's lifetime. */
+typedef struct dap_model {
+    int32_t n_q_heads;             /* Hq > 0 */
+    int32_t n_kv_heads;            /* Hkv > 0, Hq % Hkv == 0, Hq / Hkv <= 16 */
+    int32_t head_dim;              /* D: 64, 96 or 128 */
+    int32_t page_size;             /* must be 64 */
+    int32_t window;                /* 0: none; W > 0: a query at p sees keys p-W < j <= p */
+    int32_t max_position;          /* positions lie in [0, max_position) */
+    double rope_theta;             /* rotary base, > 0 */
+    int32_t llama3;                /* nonzero: llama3 three-band frequency rescale */
+    double llama3_factor;          /* e.g. 8 */
+    double llama3_low_freq_factor; /* e.g. 1 */
+    double llama3_high_freq_factor;/* e.g. 4 */
+    double llama3_original_max_position; /* e.g. 8192 */
+    int32_t qk_norm;               /* nonzero: per-head RMSNorm of q and k before rope */
+    double qk_norm_eps;            /* e.g. 1e-6 */
+} dap_model;
+
+typedef struct dap_handle dap_handle;
+
+/* Build a handle on the current HIP device: checks the constants, builds
+ * the frequency table in float64 on the host and uploads it.
+ * Frequency table ("Phi-3 Mini 4K Instruct" files, src/rope.linnet, tables):
+ * f[i] = theta^(-2i/D), i < D/2. llama3 ("Llama 3.1 8B Instruct", rope
+ * scaling paragraph): wavelength 2*pi/f above original/low_freq_factor ->
+ * f/factor; below original/high_freq_factor -> f; in between the linear
+ * blend (1-s) f/factor + s f with s = (original/wavelength - low_freq_factor)
+ * / (high_freq_factor - low_freq_factor). */
+int dap_create(const dap_model* model, dap_handle** out);
+void dap_destroy(dap_handle* handle);
+const char* dap_last_error(void);
+
+/* Validate mode (default off): see the conventions above. */
+int dap_set_validate(dap_handle* handle, int on);
+
+/* Copy the handle's float64 frequency table (n must be head_dim/2) to host memory. */
+int dap_inv_freq(const dap_handle* handle, double* out, int32_t n);
+
+/*
+ * Fused QK-norm + rope + page write.
+ * ("Phi-3 Mini 4K Instruct" files, src/attention.linnet: prefill_packed and
+ * decode_rows slice the fused projection q, k, v, rope q and k, and write k
+ * and v at each token's row and position; "Qwen3-4B": QK-norm of each
+ * head's slice before rope; "Mistral 7B Instruct v0.3", Entries:
+ * prefill_paged writes each token at its place in the pool.)
+ *
+ * q, k, v   : token t's Hq*D, Hkv*D and Hkv*D pre-rope values start at
+ *             q + t*ld_in, k + t*ld_in, v + t*ld_in (for a fused qkv row:
+ *             k = q + Hq*D, v = q + (Hq+Hkv)*D). Head h owns columns
+ *             h*D .. h*D+D-1. ld_in >= the widest slice, multiple of 8.
+ * positions : [n_tokens] int32, each in [0, max_position).
+ * rows      : [n_tokens] int32 table row of each token (ignored if slots).
+ * slots     : [n_tokens] int32 pool slot of each token, or NULL to use the
+ *             table: slot = table[rows[t]*table_ld + p/64]*64 + p%64.
+ *             Slots must be distinct within one call (else which write wins
+ *             is unspecified).
+ * q_gain, k_gain : [D] bf16 gains, required iff the model has qk_norm.
+ * q_out     : [n_tokens][ld_q_out] bf16, roped (and normed) q; may equal q
+ *             only if ld_q_out == ld_in.
+ * k_pool, v_pool : the pools; roped (and normed) k and raw v are stored at
+ *             each token's slot; nothing else in the pools changes.
+ * Arithmetic: norm, angle p*f[i], sin/cos and rotation in float64; one
+ * round-to-nearest-even to bf16 at the end.
+ */
+int dap_rope_qknorm_write_pages(dap_handle* handle,
+    const uint16_t* q, const uint16_t* k, const uint16_t* v, int64_t ld_in,
+    int32_t n_tokens, const int32_t* positions, const int32_t* rows, const int32_t* slots,
+    const int32_t* table, int32_t table_ld, int32_t n_table_rows,
+    const uint16_t* q_gain, const uint16_t* k_gain,
+    uint16_t* q_out, int64_t ld_q_out,
+    uint16_t* k_pool, uint16_t* v_pool, int32_t n_pages, void* stream);
+
+/*
+ * Packed prefill over pages.
+ * ("Phi-3 Mini 4K Instruct" files, src/attention.linnet: prefill_packed's
+ * `own` mask and window_mask; "Mistral 7B Instruct v0.3", Entries:
+ * prefill_paged attends each token over its row's pages up to its position.)
+ *
+ * Token t (row r = segments[t], position p = positions[t]) and query head h:
+ *   out[t,h] = sum_{j in J} softmax_j(q[t,h] . K[r, h/g, j] / sqrt(D)) V[r, h/g, j]
+ * with J = {j : max(0, p-W+1) <= j <= p} (all j <= p without a window) and
+ * g = Hq/Hkv. Keys are read through table row r, so a prompt sees its own
+ * row's earlier pages (chunks, shared prefixes) and nothing of other rows.
+ * Tokens may come in any order; consecutive tokens with the same segment are
+ * processed together (best performance: each prompt's tokens contiguous).
+ * q   : [n_tokens][ld_q] bf16 (roped), out : [n_tokens][ld_out] bf16.
+ * n_segments : an upper bound on the number of runs of equal consecutive
+ *             segment ids (the number of prompts in the pack); it only
+ *             sizes the launch.
+ * workspace  : device memory of at least dap_prefill_workspace_bytes().
+ * bf16 inputs, fp32 MFMA accumulation and softmax, bf16 output.
+ */
+size_t dap_prefill_workspace_bytes(const dap_handle* handle, int32_t n_tokens, int32_t n_segments);
+int dap_attn_prefill_packed(dap_handle* handle,
+    const uint16_t* q, int64_t ld_q, int32_t n_tokens,
+    const int32_t* positions, const int32_t* segments, int32_t n_segments,
+    const int32_t* table, int32_t table_ld, int32_t n_table_rows,
+    const uint16_t* k_pool, const uint16_t* v_pool, int32_t n_pages,
+    uint16_t* out, int64_t ld_out,
+    void* workspace, size_t workspace_bytes, void* stream);
+
+/*
+ * Decode over pages: one query token per row.
+ * ("Mistral 7B Instruct v0.3", Entries: decode_paged is decode_rows over
+ * pages; "Phi-3 Mini 4K Instruct" files, src/attention.linnet: decode_rows'
+ * `seen` mask.)
+ *
+ * Row b (table row rows ? rows[b] : b, position p = positions[b]): the same
+ * formula as the prefill for its one token. Keys are split into chunks of
+ * pages processed in parallel; each chunk keeps a float32 running max,
+ * sum and weighted V sum, and the last chunk of each (row, kv head) to
+ * finish merges them exactly (max-shifted rescale) and rounds to bf16, all
+ * in one kernel launch.
+ * q : [n_rows][ld_q] bf16 (roped), out : [n_rows][ld_out] bf16.
+ * workspace : at least dap_decode_workspace_bytes(handle, n_rows) bytes,
+ *             zero-filled before its first use. It starts with a fixed-size
+ *             area of per-(row, kv head) counters that every completed call
+ *             returns to zero, so one workspace serves all later calls of
+ *             any row count up to the one it was sized for, one call at a
+ *             time. n_rows is at most 65535.
+ */
+size_t dap_decode_workspace_bytes(const dap_handle* handle, int32_t n_rows);
+int dap_attn_decode_paged(dap_handle* handle,
+    const uint16_t* q, int64_t ld_q, int32_t n_rows,
+    const int32_t* positions, const int32_t* rows,
+    const int32_t* table, int32_t table_ld, int32_t n_table_rows,
+    const uint16_t* k_pool, const uint16_t* v_pool, int32_t n_pages,
+    uint16_t* out, int64_t ld_out,
+    void* workspace, size_t workspace_bytes, void* stream);
+
+/*
+ * One step over pages: packed prompts and one decode token per row in one
+ * call. ("Mistral 7B Instruct v0.3", Entries: step_paged is prefill_paged
+ * and decode_paged in one pass; "Phi-3 Mini 4K Instruct" files,
+ * src/attention.linnet, step_packed: every token's k and v are written
+ * first, then the prompts attend and each row's step attends over its row.)
+ *
+ * Tokens 0..n_prompt-1 are prompt tokens, tokens n_prompt..n_prompt+n_step-1
+ * the decode tokens. rows[t] is every token's table row (for prompt tokens
+ * also its segment); positions, rows, slots (nullable) cover all tokens.
+ * Runs the write over all tokens, then the packed prefill on the prompt
+ * tokens and the decode on the step tokens, reading q from q_out.
+ * out : [n_prompt + n_step][ld_out] bf16.
+ * workspace : at least dap_step_workspace_bytes() bytes, zero-filled before
+ *             its first use (it holds the decode workspace).
+ */
+size_t dap_step_workspace_bytes(const dap_handle* handle, int32_t n_prompt, int32_t n_segments,
+                                int32_t n_step);
+int dap_step_paged(dap_handle* handle,
+    const uint16_t* q, const uint16_t* k, const uint16_t* v, int64_t ld_in,
+    int32_t n_prompt, int32_t n_segments, int32_t n_step,
+    const int32_t* positions, const int32_t* rows, const int32_t* slots,
+    const int32_t* table, int32_t table_ld, int32_t n_table_rows,
+    const uint16_t* q_gain, const uint16_t* k_gain,
+    uint16_t* q_out, int64_t ld_q_out,
+    uint16_t* k_pool, uint16_t* v_pool, int32_t n_pages,
+    uint16_t* out, int64_t ld_out,
+    void* workspace, size_t workspace_bytes, void* stream);
+
+/*
+ * Kernel timing, for measurement (default off; not one of the pages'
+ * operations). While on, every kernel the library launches is bracketed by
+ * a pair of hipEvents recorded on its launch stream; dap_profile_read
+ * waits for the pending events and reports, per kernel kind, the summed
+ * elapsed milliseconds and the number of launches since the last reset.
+ * Turning it on creates the events (an allocation: do it outside timed or
+ * captured code); at most 1024 launches are kept pending, beyond which the
+ * oldest is waited for and folded in.
+ */
+enum {
+    DAP_KERNEL_WRITE = 0,          /* rope_qknorm_write_pages */
+    DAP_KERNEL_PREFILL_TILES = 1,  /* the prefill's tile-list pass */
+    DAP_KERNEL_PREFILL = 2,        /* the prefill's attention kernel */
+    DAP_KERNEL_DECODE = 3,         /* the decode kernel */
+    DAP_N_KERNELS = 4
+};
+int dap_set_profiling(dap_handle* handle, int on);
+int dap_profile_read(dap_handle* handle, double* total_ms, int64_t* launches, int reset);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* DAP_H */

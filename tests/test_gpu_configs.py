@@ -1,0 +1,204 @@
+"""GPU parity on the five model-shaped workloads at full size, in the launch
+configuration the benchmark times (same entries, same shapes).
+
+Every token's written q_out and K are compared bit for bit (>= 99.99%
+identical, all within 1 ulp) and V exactly; attention outputs are compared
+element by element on sampled tokens/rows the oracle computes one by one
+(including the first and last of every prompt and the longest and shortest
+rows), and on all outputs where the oracle is cheap enough."""
+import numpy as np
+import pytest
+import torch
+
+import decoder_attention_paged_amd as dap
+import workloads as W
+from oracle import attention, bf16, pages
+
+from parity import (OraclePool, check_bits, check_close, device_pools, handle_for, oracle_attention,
+                    oracle_front, to_np_bits, torch_i32)
+
+pytestmark = pytest.mark.gpu
+
+
+def _split(qkv, m):
+    D, hq, hkv = m.head_dim, m.n_q_heads, m.n_kv_heads
+    return qkv[:, :hq * D], qkv[:, hq * D:(hq + hkv) * D], qkv[:, (hq + hkv) * D:]
+
+
+def _gains(wl):
+    if not wl.model.qk_norm_eps:
+        return None, None
+    g = (wl.gains("q", "cuda"), wl.gains("k", "cuda"))
+    return g, (to_np_bits(g[0]), to_np_bits(g[1]))
+
+
+def _check_written(wl, kp, vp, slots, k_bits, v_bits, what):
+    kg, vg = dap.gather_slots(kp, vp, slots)
+    check_bits(to_np_bits(kg), k_bits, what + " K")
+    assert np.array_equal(to_np_bits(vg), v_bits), what + " V must be a bit copy"
+
+
+def test_phi3_prefill_then_decode_loop():
+    wl = W.phi3()
+    m = wl.model
+    h = handle_for(m)
+    kp, vp = device_pools(wl)
+    op = OraclePool(wl, "cuda")
+    table = torch_i32(wl.table)
+    T = wl.n_pre
+    qkv = wl.qkv("prompt", T, "cuda")
+    pos, seg = torch_i32(wl.pre_positions), torch_i32(wl.pre_segments)
+    q_out = h.rope_qknorm_write_pages(*_split(qkv, m), pos, kp, vp, rows=seg, table=table)
+    out = h.attn_prefill_packed(q_out, pos, seg, table, kp, vp, n_segments=4)
+    torch.cuda.synchronize()
+    _, q_bits, k_bits, v_bits = oracle_front(wl, to_np_bits(qkv), wl.pre_positions)
+    check_bits(to_np_bits(q_out).reshape(q_bits.shape), q_bits, "prompt q_out")
+    slots = pages.slot_of(wl.table, wl.pre_segments, wl.pre_positions)
+    _check_written(wl, kp, vp, slots, k_bits, v_bits, "prompt")
+    op.write(slots, k_bits, v_bits)
+    # sampled prompt tokens: both ends of every prompt, the window edge, random
+    rng = np.random.default_rng(0)
+    starts = np.cumsum((0,) + W.PHI3_PROMPTS)
+    pick = set(rng.choice(T, 200, replace=False).tolist())
+    for s, e in zip(starts[:-1], starts[1:]):
+        pick |= {int(s), int(s) + 1, int(e) - 1, int(e) - 2}
+    pick |= {int(starts[2]) + 2046, int(starts[2]) + 2047}        # third prompt crosses the window
+    pick = np.array(sorted(pick))
+    ref = oracle_attention(wl, op, bf16.to_f64(q_bits[pick]), wl.pre_positions[pick], wl.pre_segments[pick])
+    check_close(to_np_bits(out)[pick], ref, "phi3 prefill (sampled)")
+
+    # decode loop: every step writes its active rows' tokens and attends
+    steps = W.phi3_decode_schedule()
+    sample_steps = {0, 1, 463, 464, 465, 1000, 1463, 1464, 1465, 1975, 1976, 1977, 2400, 2488}
+    ws = h.workspace(h.decode_workspace_bytes(4))
+    kept = {}
+    all_slots, all_tok = [], []
+    for t, (rows, positions) in enumerate(steps):
+        x = wl.qkv("step", len(rows), "cuda", row0=4 * t)
+        tp, tr = torch_i32(positions), torch_i32(rows)
+        qo = h.rope_qknorm_write_pages(*_split(x, m), tp, kp, vp, rows=tr, table=table)
+        o = h.attn_decode_paged(qo, tp, table, kp, vp, rows=tr, workspace=ws)
+        if t in sample_steps:
+            kept[t] = (x.clone(), o.clone())
+        all_tok.append((t, rows, positions))
+    torch.cuda.synchronize()
+    # the oracle writes every decode token (its own k/v) and checks sampled steps
+    for t, rows, positions in all_tok:
+        x = wl.qkv("step", len(rows), "cpu", row0=4 * t).numpy().view(np.uint16)
+        _, qb, kb, vb = oracle_front(wl, x, positions)
+        s = pages.slot_of(wl.table, rows, positions)
+        op.write(s, kb, vb)
+        if t in kept:
+            assert np.array_equal(to_np_bits(kept[t][0]), x)
+            ref = oracle_attention(wl, op, bf16.to_f64(qb), positions, rows)
+            check_close(to_np_bits(kept[t][1]), ref, f"phi3 decode step {t}")
+    # read-only measurement call: all four rows at 3000
+    q = W.normal_matrix(wl.key("q", "final"), 4, m.n_q_heads * m.head_dim, "cuda")
+    p3000 = np.full(4, 3000, np.int32)
+    o = h.attn_decode_paged(q, torch_i32(p3000), table, kp, vp, workspace=ws)
+    torch.cuda.synchronize()
+    ref = oracle_attention(wl, op, bf16.to_f64(to_np_bits(q)).reshape(4, m.n_q_heads, m.head_dim),
+                           p3000, np.arange(4))
+    check_close(to_np_bits(o), ref, "phi3 decode at 3000")
+    # every position 0..3000 of every row, bit for bit against the oracle's pool
+    for r in range(4):
+        sl = pages.slot_of(wl.table, np.full(3001, r), np.arange(3001))
+        kg, vg = dap.gather_slots(kp, vp, sl)
+        ko = np.stack([op.read_page(int(s) // 64)[0][:, int(s) % 64] for s in sl])
+        vo = np.stack([op.read_page(int(s) // 64)[1][:, int(s) % 64] for s in sl])
+        check_bits(to_np_bits(kg), bf16.from_f64(ko), f"row {r} K after the loop")
+        assert np.array_equal(to_np_bits(vg), bf16.from_f64(vo))
+
+
+def test_mistral_decode():
+    wl = W.mistral()
+    m = wl.model
+    h = handle_for(m)
+    kp, vp = device_pools(wl)
+    table = torch_i32(wl.table)
+    R = wl.n_dec
+    qkv = wl.qkv("step", R, "cuda")
+    pos, rows = torch_i32(wl.dec_positions), torch_i32(wl.dec_rows)
+    q_out = h.rope_qknorm_write_pages(*_split(qkv, m), pos, kp, vp, rows=rows, table=table)
+    out = h.attn_decode_paged(q_out, pos, table, kp, vp)
+    torch.cuda.synchronize()
+    _, q_bits, k_bits, v_bits = oracle_front(wl, to_np_bits(qkv), wl.dec_positions)
+    check_bits(to_np_bits(q_out).reshape(q_bits.shape), q_bits, "q_out")
+    slots = pages.slot_of(wl.table, wl.dec_rows, wl.dec_positions)
+    _check_written(wl, kp, vp, slots, k_bits, v_bits, "new token")
+    op = OraclePool(wl, "cuda")
+    op.write(slots, k_bits, v_bits)
+    order = np.argsort(wl.dec_positions)
+    pick = np.unique(np.concatenate([order[:3], order[-3:], np.random.default_rng(1).choice(R, 6, replace=False)]))
+    ref = oracle_attention(wl, op, bf16.to_f64(q_bits[pick]), wl.dec_positions[pick], wl.dec_rows[pick])
+    check_close(to_np_bits(out)[pick], ref, "mistral decode (sampled rows)")
+    # peaky variant on the same rows: q scaled by 4
+    q4 = (q_out.view(torch.bfloat16).float() * 4).to(torch.bfloat16)
+    out4 = h.attn_decode_paged(q4, pos, table, kp, vp)
+    torch.cuda.synchronize()
+    ref4 = oracle_attention(wl, op, 4 * bf16.to_f64(q_bits[pick]), wl.dec_positions[pick], wl.dec_rows[pick])
+    check_close(to_np_bits(out4)[pick], ref4, "mistral decode peaky")
+
+
+def test_llama31_chunked_prefill():
+    wl = W.llama31()
+    m = wl.model
+    h = handle_for(m)
+    kp, vp = device_pools(wl)
+    table = torch_i32(wl.table)
+    T = wl.n_pre
+    qkv = wl.qkv("chunk", T, "cuda")
+    pos, seg = torch_i32(wl.pre_positions), torch_i32(wl.pre_segments)
+    q_out = h.rope_qknorm_write_pages(*_split(qkv, m), pos, kp, vp, rows=seg, table=table)
+    out = h.attn_prefill_packed(q_out, pos, seg, table, kp, vp, n_segments=1)
+    torch.cuda.synchronize()
+    _, q_bits, k_bits, v_bits = oracle_front(wl, to_np_bits(qkv), wl.pre_positions)
+    check_bits(to_np_bits(q_out).reshape(q_bits.shape), q_bits, "q_out")
+    slots = pages.slot_of(wl.table, wl.pre_segments, wl.pre_positions)
+    _check_written(wl, kp, vp, slots, k_bits, v_bits, "chunk")
+    op = OraclePool(wl, "cuda")
+    op.write(slots, k_bits, v_bits)
+    rng = np.random.default_rng(2)
+    pick = np.unique(np.concatenate([np.arange(4), np.arange(T - 4, T), [63, 64, 4095, 4096],
+                                     rng.choice(T, 24, replace=False)]))
+    ref = oracle_attention(wl, op, bf16.to_f64(q_bits[pick]), wl.pre_positions[pick], wl.pre_segments[pick])
+    check_close(to_np_bits(out)[pick], ref, "llama31 prefill (sampled)")
+
+
+def test_qwen3_step_paged():
+    wl = W.qwen3()
+    m = wl.model
+    h = handle_for(m)
+    kp, vp = device_pools(wl)
+    table = torch_i32(wl.table)
+    P, R = wl.n_pre, wl.n_dec
+    qkv = wl.qkv("step", P + R, "cuda")
+    pos = torch_i32(np.concatenate([wl.pre_positions, wl.dec_positions]))
+    rows = torch_i32(np.concatenate([wl.pre_segments, wl.dec_rows]))
+    (g, g_np) = _gains(wl)
+    q_out, out = h.step_paged(*_split(qkv, m), pos, rows, table, kp, vp, n_prompt=P, n_segments=8,
+                              q_gain=g[0], k_gain=g[1])
+    torch.cuda.synchronize()
+    all_pos = np.concatenate([wl.pre_positions, wl.dec_positions])
+    all_rows = np.concatenate([wl.pre_segments, wl.dec_rows])
+    _, q_bits, k_bits, v_bits = oracle_front(wl, to_np_bits(qkv), all_pos, g_np)
+    check_bits(to_np_bits(q_out).reshape(q_bits.shape), q_bits, "q_out")
+    slots = pages.slot_of(wl.table, all_rows, all_pos)
+    _check_written(wl, kp, vp, slots, k_bits, v_bits, "step")
+    op = OraclePool(wl, "cuda")
+    op.write(slots, k_bits, v_bits)
+    # every prompt token (each sees at most 384 keys)
+    ref = oracle_attention(wl, op, bf16.to_f64(q_bits[:P]), wl.pre_positions, wl.pre_segments)
+    check_close(to_np_bits(out)[:P], ref, "qwen3 prefill part (all 2048 tokens)")
+    # sampled decode rows: shortest, longest, random
+    order = np.argsort(wl.dec_positions)
+    pick = np.unique(np.concatenate([order[:3], order[-3:], np.random.default_rng(3).choice(R, 8, replace=False)]))
+    ref = oracle_attention(wl, op, bf16.to_f64(q_bits[P + pick]), wl.dec_positions[pick], wl.dec_rows[pick])
+    check_close(to_np_bits(out)[P + pick], ref, "qwen3 decode part (sampled rows)")
+    # the composition equals the three entries called one after another
+    ws_d = h.workspace(h.decode_workspace_bytes(R))
+    o_pre = h.attn_prefill_packed(q_out[:P], pos[:P], rows[:P], table, kp, vp, n_segments=8)
+    o_dec = h.attn_decode_paged(q_out[P:], pos[P:], table, kp, vp, rows=rows[P:], workspace=ws_d)
+    torch.cuda.synchronize()
+    assert torch.equal(o_pre.view(torch.int16), out[:P].view(torch.int16))
+    assert torch.equal(o_dec.view(torch.int16), out[P:].view(torch.int16))

@@ -1,0 +1,231 @@
+"""GPU parity of each entry on small seeded inputs that span several tiles,
+ragged tails, page edges, windows and every supported head shape.
+
+Inputs come straight from the generators (bf16 N(0,1) queries, pools of
+generated pages), so both sides see identical bits; the oracle is the fp64
+definition in oracle/."""
+import zlib
+
+import numpy as np
+import pytest
+import torch
+
+import decoder_attention_paged_amd as dap
+import workloads as W
+from oracle import attention, bf16, core, pages
+
+from parity import (OraclePool, check_bits, check_close, device_pools, handle_for, oracle_front,
+                    to_np_bits, torch_i32)
+
+pytestmark = pytest.mark.gpu
+
+
+def _model(hq, hkv, d, window=0, max_position=4096, theta=1e4, llama3=None, eps=None):
+    return W.ModelShape(f"unit-{hq}-{hkv}-{d}-{window}", hq, hkv, d, theta, window=window, llama3=llama3,
+                        qk_norm_eps=eps, max_position=max_position)
+
+
+def _workload(model, n_rows, n_pages_per_row, tag, shared=0):
+    """Rows with their own pages from one seeded permutation."""
+    rng = np.random.default_rng(zlib.crc32(tag.encode()))
+    n_pages = n_rows * n_pages_per_row
+    perm = rng.permutation(n_pages).astype(np.int32)
+    table = perm.reshape(n_rows, n_pages_per_row)
+    return W.Workload(tag, model, n_pages, table)
+
+
+def _queries(wl, n, scale=1.0, tag="q"):
+    q = W.normal_matrix(wl.key(tag), n, wl.model.n_q_heads * wl.model.head_dim, "cuda")
+    if scale != 1.0:
+        q = (q.view(torch.bfloat16).float() * scale).to(torch.bfloat16).view(torch.int16)
+    return q
+
+
+DECODE_SHAPES = [
+    (4, 2, 64, 0), (32, 32, 96, 2047), (32, 8, 128, 0), (8, 1, 128, 0), (16, 1, 64, 100), (4, 4, 96, 0),
+]
+
+
+@pytest.mark.parametrize("hq,hkv,d,window", DECODE_SHAPES)
+@pytest.mark.parametrize("peaky", [False, True])
+def test_decode_matches_oracle(hq, hkv, d, window, peaky):
+    model = _model(hq, hkv, d, window, max_position=4096)
+    wl = _workload(model, 6, 64, f"dec-{hq}-{hkv}-{d}-{window}")
+    kp, vp = device_pools(wl)
+    positions = np.array([0, 63, 64, 1000, 2047, 4095], np.int32)
+    q = _queries(wl, 6, 4.0 if peaky else 1.0)
+    h = handle_for(model)
+    out = h.attn_decode_paged(q, torch_i32(positions), torch_i32(wl.table), kp, vp)
+    torch.cuda.synchronize()
+    op = OraclePool(wl, "cuda")
+    ref = attention.paged(bf16.to_f64(to_np_bits(q)).reshape(6, hq, d), positions, np.arange(6), wl.table,
+                          op.read_page, window)
+    check_close(to_np_bits(out), ref, f"decode {hq}/{hkv}/{d} w{window}")
+
+
+def test_decode_rows_indirection_and_split_invariance():
+    model = _model(32, 8, 128, 0, max_position=4096)
+    wl = _workload(model, 8, 64, "dec-rows")
+    kp, vp = device_pools(wl)
+    rows = np.array([7, 2, 2, 5], np.int32)
+    positions = np.array([4095, 4000, 130, 64], np.int32)
+    q = _queries(wl, 4)
+    outs = []
+    for max_pos in (4096, 65536, 1 << 20):           # different page chunking
+        m2 = _model(32, 8, 128, 0, max_position=max_pos)
+        h = handle_for(m2)
+        outs.append(h.attn_decode_paged(q, torch_i32(positions), torch_i32(wl.table), kp, vp,
+                                        rows=torch_i32(rows)).view(torch.bfloat16).float())
+    torch.cuda.synchronize()
+    op = OraclePool(wl, "cuda")
+    ref = attention.paged(bf16.to_f64(to_np_bits(q)).reshape(4, 32, 128), positions, rows, wl.table,
+                          op.read_page, 0)
+    check_close(to_np_bits(outs[0].to(torch.bfloat16)), ref, "decode rows")
+    for o in outs[1:]:
+        assert torch.allclose(o, outs[0], atol=1e-2, rtol=0)
+
+
+PREFILL_SHAPES = [(4, 2, 64, 0), (32, 32, 96, 2047), (32, 8, 128, 0), (8, 8, 128, 40), (8, 2, 96, 0)]
+
+
+@pytest.mark.parametrize("hq,hkv,d,window", PREFILL_SHAPES)
+@pytest.mark.parametrize("peaky", [False, True])
+def test_prefill_packed_matches_oracle(hq, hkv, d, window, peaky):
+    model = _model(hq, hkv, d, window, max_position=1024)
+    wl = _workload(model, 5, 16, f"pre-{hq}-{hkv}-{d}-{window}")
+    kp, vp = device_pools(wl)
+    # ragged prompts: a single token, sub-tile, exact tile, multi-tile, and a
+    # chunk continuing after a prefix at a page-unaligned position
+    spec = [(0, 0, 1), (1, 0, 37), (2, 0, 128), (3, 0, 261), (4, 300, 200)]
+    pos = np.concatenate([np.arange(s, s + n) for _, s, n in spec]).astype(np.int32)
+    seg = np.concatenate([np.full(n, r) for r, _, n in spec]).astype(np.int32)
+    T = len(pos)
+    q = _queries(wl, T, 4.0 if peaky else 1.0)
+    h = handle_for(model)
+    out = h.attn_prefill_packed(q, torch_i32(pos), torch_i32(seg), torch_i32(wl.table), kp, vp,
+                                n_segments=len(spec))
+    torch.cuda.synchronize()
+    op = OraclePool(wl, "cuda")
+    ref = attention.paged(bf16.to_f64(to_np_bits(q)).reshape(T, hq, d), pos, seg, wl.table, op.read_page, window)
+    check_close(to_np_bits(out), ref, f"prefill {hq}/{hkv}/{d} w{window}")
+
+
+def test_prefill_unsorted_tokens_and_repeated_segments():
+    """Tokens of one prompt need not be contiguous or sorted: each token sees
+    its own row up to its own position."""
+    model = _model(32, 8, 128, 0, max_position=1024)
+    wl = _workload(model, 3, 16, "pre-shuffle")
+    kp, vp = device_pools(wl)
+    rng = np.random.default_rng(5)
+    pos = rng.integers(0, 1024, 300).astype(np.int32)
+    seg = np.repeat(rng.integers(0, 3, 30), 10).astype(np.int32)
+    q = _queries(wl, 300)
+    h = handle_for(model)
+    out = h.attn_prefill_packed(q, torch_i32(pos), torch_i32(seg), torch_i32(wl.table), kp, vp,
+                                n_segments=30)
+    torch.cuda.synchronize()
+    op = OraclePool(wl, "cuda")
+    ref = attention.paged(bf16.to_f64(to_np_bits(q)).reshape(300, 32, 128), pos, seg, wl.table, op.read_page, 0)
+    check_close(to_np_bits(out), ref, "prefill shuffled")
+
+
+WRITE_MODELS = [
+    _model(4, 2, 64, 0, 4096, theta=1e4),
+    _model(32, 32, 96, 2047, 4096, theta=1e4),
+    _model(32, 8, 128, 0, 65536, theta=5e5, llama3=(8.0, 1.0, 4.0, 8192.0)),
+    _model(32, 8, 128, 0, 40960, theta=1e6, eps=1e-6),
+]
+
+
+@pytest.mark.parametrize("model", WRITE_MODELS, ids=lambda m: m.name)
+@pytest.mark.parametrize("explicit_slots", [False, True])
+def test_write_matches_oracle_bits(model, explicit_slots):
+    n_rows = 4
+    ppr = model.max_position // 64
+    wl = _workload(model, n_rows, ppr, "wr-" + model.name)
+    kp, vp = device_pools(wl)
+    k_before, v_before = kp.clone(), vp.clone()
+    rng = np.random.default_rng(9)
+    T = 300
+    rows = rng.integers(0, n_rows, T).astype(np.int32)
+    # distinct (row, position) pairs, positions across the whole range
+    flat = rng.choice(n_rows * model.max_position, T, replace=False)
+    rows, positions = (flat // model.max_position).astype(np.int32), (flat % model.max_position).astype(np.int32)
+    qkv = W.normal_matrix(wl.key("qkv"), T, model.qkv_width, "cuda")
+    D, hq, hkv = model.head_dim, model.n_q_heads, model.n_kv_heads
+    gains = None
+    if model.qk_norm_eps:
+        gains = (wl.gains("q", "cuda"), wl.gains("k", "cuda"))
+    slots = pages.slot_of(wl.table, rows, positions)
+    h = handle_for(model)
+    q_out = h.rope_qknorm_write_pages(
+        qkv[:, :hq * D], qkv[:, hq * D:(hq + hkv) * D], qkv[:, (hq + hkv) * D:], torch_i32(positions), kp, vp,
+        rows=None if explicit_slots else torch_i32(rows),
+        slots=torch_i32(slots) if explicit_slots else None,
+        table=None if explicit_slots else torch_i32(wl.table),
+        q_gain=gains[0] if gains else None, k_gain=gains[1] if gains else None)
+    torch.cuda.synchronize()
+    g_np = (to_np_bits(gains[0]), to_np_bits(gains[1])) if gains else None
+    _, q_bits, k_bits, v_bits = oracle_front(wl, to_np_bits(qkv), positions, g_np)
+    check_bits(to_np_bits(q_out).reshape(T, hq, D), q_bits, "q_out")
+    kg, vg = dap.gather_slots(kp, vp, slots)
+    check_bits(to_np_bits(kg), k_bits, "K pages")
+    assert np.array_equal(to_np_bits(vg), v_bits), "V pages must be a bit copy"
+    # nothing else in the pools changed
+    s = torch.as_tensor(slots, device="cuda")
+    k_before[s // 64, :, s % 64, :] = kp[s // 64, :, s % 64, :]
+    v_before[s // 64, :, :, s % 64] = vp[s // 64, :, :, s % 64]
+    assert torch.equal(k_before.view(torch.int16), kp.view(torch.int16))
+    assert torch.equal(v_before.view(torch.int16), vp.view(torch.int16))
+
+
+def test_write_in_place_q():
+    model = _model(32, 8, 128, 0, 512, theta=1e6, eps=1e-6)
+    wl = _workload(model, 2, 8, "wr-inplace")
+    kp, vp = device_pools(wl)
+    T = 64
+    positions = np.arange(100, 164, dtype=np.int32)
+    rows = np.zeros(T, np.int32)
+    qkv = W.normal_matrix(wl.key("qkv"), T, model.qkv_width, "cuda")
+    D, hq, hkv = model.head_dim, model.n_q_heads, model.n_kv_heads
+    gains = (wl.gains("q", "cuda"), wl.gains("k", "cuda"))
+    _, q_bits, _, _ = oracle_front(wl, to_np_bits(qkv), positions, (to_np_bits(gains[0]), to_np_bits(gains[1])))
+    h = handle_for(model)
+    qv = qkv[:, :hq * D]
+    h.rope_qknorm_write_pages(qv, qkv[:, hq * D:(hq + hkv) * D], qkv[:, (hq + hkv) * D:], torch_i32(positions),
+                              kp, vp, rows=torch_i32(rows), table=torch_i32(wl.table), q_out=qv,
+                              q_gain=gains[0], k_gain=gains[1])
+    torch.cuda.synchronize()
+    check_bits(to_np_bits(qv).reshape(T, hq, D), q_bits, "in-place q_out")
+
+
+def test_inv_freq_table_matches_oracle():
+    for model in WRITE_MODELS:
+        h = handle_for(model)
+        from parity import oracle_freqs
+        assert np.allclose(h.inv_freq().numpy(), oracle_freqs(model), rtol=1e-15, atol=0)
+
+
+def test_decode_workspace_reused_across_row_counts():
+    """One zeroed workspace serves calls with different row counts: each
+    call must match a call on a fresh workspace bit for bit."""
+    model = _model(32, 32, 96, 2047, max_position=4096)
+    wl = _workload(model, 4, 64, "dec-ws-reuse")
+    kp, vp = device_pools(wl)
+    h = handle_for(model)
+    table = torch_i32(wl.table)
+    ws = h.workspace(h.decode_workspace_bytes(4))
+    q = _queries(wl, 4)
+    keep = []
+    for n in (4, 1, 2, 4, 3, 1, 4):
+        pos = torch_i32(np.array([3000, 2100, 700, 4000][:n], np.int32))
+        rows = torch_i32(np.arange(n)[::-1].copy())
+        a = h.attn_decode_paged(q[:n], pos, table, kp, vp, rows=rows, workspace=ws)
+        b = h.attn_decode_paged(q[:n], pos, table, kp, vp, rows=rows)          # fresh zeroed workspace
+        keep.append((a, b, pos, rows))
+    torch.cuda.synchronize()
+    for a, b, _, _ in keep:
+        assert torch.equal(a.view(torch.int16), b.view(torch.int16))
+    # and the shared workspace's counters are all zero again
+    counters = ws[: 65535 * model.n_kv_heads * 4].view(torch.int32)
+    assert int(counters.abs().sum()) == 0
