@@ -28,7 +28,7 @@ EXPORTS = ("dap_create", "dap_destroy", "dap_last_error", "dap_set_validate", "d
            "dap_decode_workspace_bytes", "dap_attn_decode_paged", "dap_step_workspace_bytes",
            "dap_step_paged", "dap_set_profiling", "dap_profile_read")
 
-KERNELS = ("write", "prefill_tiles", "prefill", "decode")
+KERNELS = ("write", "prefill_tiles", "prefill", "decode", "decode_merge")
 
 
 class DapError(RuntimeError):

@@ -496,8 +496,7 @@ int dap_attn_decode_paged(dap_handle* h, const uint16_t* q, int64_t ld_q, int32_
                      ld_out, workspace, workspace_bytes, static_cast<hipStream_t>(stream));
 }
 
-// Step workspace: the decode workspace first (its counters persist between
-// calls at a fixed place), then the prefill's tile list (rewritten every call).
+// Step workspace: the decode's partials, then the prefill's tile list.
 size_t dap_step_workspace_bytes(const dap_handle* h, int32_t n_prompt, int32_t n_segments, int32_t n_step) {
     if (!h || n_prompt < 0 || n_step < 0) return 0;
     return align256(dap_decode_workspace_bytes(h, n_step)) + dap_prefill_workspace_bytes(h, n_prompt, n_segments);

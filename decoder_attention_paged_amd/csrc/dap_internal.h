@@ -129,16 +129,13 @@ struct AttnArgs {
 };
 
 // Decode: split count and workspace layout.
-// Workspace: [counters: kMaxDecodeRows * Hkv ints, padded to 256 B]
-//            [partials: n_rows * Hq * max_splits * (D + 2) floats]
-// The counters must be zero before the first call; every call leaves them zero.
-constexpr int kMaxDecodeRows = 65535;
+// Workspace: partials [n_rows][Hq][max_splits][D + 2] floats (o[D], m, l).
 struct DecodePlan {
     int pages_per_split;
     int max_splits;
-    size_t counter_bytes;
     size_t workspace_bytes;
 };
+constexpr int kMaxDecodeRows = 65535;
 DecodePlan decode_plan(int n_rows, int n_q_heads, int n_kv_heads, int head_dim, int window,
                        int max_position);
 hipError_t launch_decode(const AttnArgs& a, const DecodePlan& plan, void* workspace, hipStream_t s,

@@ -17,10 +17,8 @@
 //
 // Merge: a row whose range fits one chunk is finished by that workgroup.
 // Otherwise each chunk stores its fp32 (m, l, o) per head in the workspace
-// and bumps a per-(row, kv head) counter; the last chunk to arrive merges all
-// chunks with the max-shifted rescale (exactly the single-pass softmax in
-// real arithmetic), rounds to bf16 and resets the counter to zero, so one
-// launch does the whole decode and the counters stay zeroed between calls.
+// and a second, small kernel merges the chunks with the max-shifted rescale
+// (exactly the single-pass softmax in real arithmetic) and rounds to bf16.
 #include "dap_internal.h"
 
 namespace dap {
@@ -33,11 +31,33 @@ constexpr float kLog2e = 1.4426950408889634f;
 
 __device__ __forceinline__ bf16x8 as_bf16x8(u32x4 u) { return __builtin_bit_cast(bf16x8, u); }
 
-// Key (within a 64-key page) held in row i of the S block blk. Chosen so the
-// four lanes groups' S values line up with contiguous 8-key runs of the V^T
-// rows in the PV step (group g, step t holds keys 16g + 8t .. 16g + 8t + 7).
-__device__ __forceinline__ int decode_key(int blk, int i) {
-    return 16 * (i >> 2) + 8 * (blk >> 1) + 4 * (blk & 1) + (i & 3);
+// A wave works on 32-key units (half pages). In a unit, S block blk (16
+// keys) holds in A-row i the key 8*(i/4) + 4*blk + i%4, so lane group g ends
+// up with the S values of keys 8g .. 8g+7, which are the 8 contiguous keys
+// its V^T fragment covers in the PV step; K and V^T loads both read 64
+// contiguous bytes per row per instruction.
+__device__ __forceinline__ int unit_key(int blk, int i) { return 8 * (i >> 2) + 4 * blk + (i & 3); }
+
+constexpr int kMaxPagesPerSplit = 256;
+
+template <int D>
+struct UnitFrags {
+    u32x4 k[2][D / 32];   // K rows, two 16-key blocks
+    u32x4 v[D / 16];      // V^T, 16 dims x 32 keys per block
+};
+
+template <int D>
+__device__ __forceinline__ void load_unit(UnitFrags<D>& f, const uint16_t* kt, const uint16_t* vt, int half,
+                                          int col, int grp) {
+#pragma unroll
+    for (int blk = 0; blk < 2; ++blk) {
+        const uint16_t* kr = kt + (32 * half + unit_key(blk, col)) * D + 8 * grp;
+#pragma unroll
+        for (int s = 0; s < D / 32; ++s) f.k[blk][s] = *reinterpret_cast<const u32x4*>(kr + 32 * s);
+    }
+#pragma unroll
+    for (int db = 0; db < D / 16; ++db)
+        f.v[db] = *reinterpret_cast<const u32x4*>(vt + (16 * db + col) * kPage + 32 * half + 8 * grp);
 }
 
 struct RowRange {
@@ -73,14 +93,70 @@ __device__ __forceinline__ RowRange row_range(const AttnArgs& a, int b, bool fla
 }
 
 template <int D>
+struct WaveState {
+    float m, lsum;
+    f32x4 o[D / 16];
+};
+
+// One 32-key unit: S = K q^T, mask, online softmax, O^T += V^T P^T.
+template <int D>
+__device__ __forceinline__ void compute_unit(WaveState<D>& st, const UnitFrags<D>& f, const bf16x8* qf, float c,
+                                             int base, int lo, int p, int grp) {
+    f32x4 sc[2];
+#pragma unroll
+    for (int blk = 0; blk < 2; ++blk) {
+        f32x4 acc = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+        for (int s = 0; s < D / 32; ++s)
+            acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(as_bf16x8(f.k[blk][s]), qf[s], acc, 0, 0, 0);
+        sc[blk] = acc * c;
+    }
+    if (base < lo || base + 31 > p) {
+#pragma unroll
+        for (int blk = 0; blk < 2; ++blk)
+#pragma unroll
+            for (int r = 0; r < 4; ++r) {
+                const int kp = base + 8 * grp + 4 * blk + r;
+                if (kp < lo || kp > p) sc[blk][r] = -INFINITY;
+            }
+    }
+    float mx = fmaxf(fmaxf(fmaxf(sc[0][0], sc[0][1]), fmaxf(sc[0][2], sc[0][3])),
+                     fmaxf(fmaxf(sc[1][0], sc[1][1]), fmaxf(sc[1][2], sc[1][3])));
+    mx = fmaxf(mx, __shfl_xor(mx, 16));
+    mx = fmaxf(mx, __shfl_xor(mx, 32));
+    const float m_new = fmaxf(st.m, mx);      // finite: every unit computed holds a visible key
+    const float alpha = exp2f(st.m - m_new);
+    float ps = 0.f;
+    bf16x8 pf;
+#pragma unroll
+    for (int blk = 0; blk < 2; ++blk)
+#pragma unroll
+        for (int r = 0; r < 4; ++r) {
+            const float e = exp2f(sc[blk][r] - m_new);
+            ps += e;
+            pf[4 * blk + r] = (__bf16)e;
+        }
+    st.lsum = st.lsum * alpha + ps;
+    st.m = m_new;
+#pragma unroll
+    for (int db = 0; db < D / 16; ++db) {
+        st.o[db] *= alpha;
+        st.o[db] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(as_bf16x8(f.v[db]), pf, st.o[db], 0, 0, 0);
+    }
+}
+
+template <int D>
 __global__ __launch_bounds__(kDecodeThreads, 2) void decode_kernel(AttnArgs a, int pps, int max_splits,
-                                                                   float* __restrict__ ws, int* ws_counters) {
+                                                                   float* __restrict__ ws) {
     constexpr int kSteps = D / 32;     // QK k-steps of 32 dims
     constexpr int kDimBlocks = D / 16; // PV output blocks of 16 dims
 
     __shared__ float s_m[kDecodeWaves][16];
     __shared__ float s_l[kDecodeWaves][16];
-    __shared__ float s_o[kDecodeWaves][D][17];
+    __shared__ int s_pg[kMaxPagesPerSplit];
+    // per-wave O for the cross-wave merge, [wave][dim][head] for the g real
+    // heads only (sized at launch: 4 * D * g floats)
+    extern __shared__ float s_o[];
 
     const int split = blockIdx.x;
     const int kh = blockIdx.y;
@@ -96,8 +172,17 @@ __global__ __launch_bounds__(kDecodeThreads, 2) void decode_kernel(AttnArgs a, i
     const int n_splits = (rr.n_pg + pps - 1) / pps;
     if (split >= n_splits) return;
     const int j0 = rr.first_pg + split * pps;
-    const int j1 = min(j0 + pps, rr.first_pg + rr.n_pg);
+    const int n_local = min(pps, rr.first_pg + rr.n_pg - j0);
     const int G = a.n_q_heads / a.n_kv_heads;
+
+    // this chunk's page ids, once, into LDS (-1 marks an out-of-range id)
+    const int* trow = a.table + (long long)rr.row * a.table_ld;
+    for (int i = tid; i < n_local; i += kDecodeThreads) {
+        const int pg = trow[j0 + i];
+        const bool ok = pg >= 0 && pg < a.n_pages;
+        if (!ok) atomicOr(a.err, kErrPage);
+        s_pg[i] = ok ? pg : -1;
+    }
 
     // q^T as the B operand: column = head, rows = dims 32s + 8*grp .. +7.
     bf16x8 qf[kSteps];
@@ -111,97 +196,55 @@ __global__ __launch_bounds__(kDecodeThreads, 2) void decode_kernel(AttnArgs a, i
             qf[s] = as_bf16x8(u);
         }
     }
+    __syncthreads();
 
     const float c = kLog2e / sqrtf((float)D);
-    float m = -INFINITY;
-    float lsum = 0.f;
-    f32x4 o[kDimBlocks];
+    WaveState<D> st;
+    st.m = -INFINITY;
+    st.lsum = 0.f;
 #pragma unroll
-    for (int db = 0; db < kDimBlocks; ++db) o[db] = f32x4{0.f, 0.f, 0.f, 0.f};
+    for (int db = 0; db < kDimBlocks; ++db) st.o[db] = f32x4{0.f, 0.f, 0.f, 0.f};
 
-    const int* trow = a.table + (long long)rr.row * a.table_ld;
-    for (int jj = j0 + wave; jj < j1; jj += kDecodeWaves) {
-        const int pg = trow[jj];
-        if (pg < 0 || pg >= a.n_pages) {
-            atomicOr(a.err, kErrPage);
-            continue;
-        }
-        const uint16_t* kt = a.k_pool + ((long long)pg * a.n_kv_heads + kh) * (kPage * D);
-        const uint16_t* vt = a.v_pool + ((long long)pg * a.n_kv_heads + kh) * (kPage * D);
-
-        u32x4 kf[4][kSteps];
-#pragma unroll
-        for (int blk = 0; blk < 4; ++blk) {
-            const uint16_t* kr = kt + decode_key(blk, col) * D + 8 * grp;
-#pragma unroll
-            for (int s = 0; s < kSteps; ++s) kf[blk][s] = *reinterpret_cast<const u32x4*>(kr + 32 * s);
-        }
-        u32x4 vf[2][kDimBlocks];
-#pragma unroll
-        for (int t = 0; t < 2; ++t) {
-#pragma unroll
-            for (int db = 0; db < kDimBlocks; ++db)
-                vf[t][db] = *reinterpret_cast<const u32x4*>(vt + (16 * db + col) * kPage + 16 * grp + 8 * t);
-        }
-
-        // S = K q^T, 16 keys per block
-        f32x4 sc[4];
-#pragma unroll
-        for (int blk = 0; blk < 4; ++blk) {
-            f32x4 acc = {0.f, 0.f, 0.f, 0.f};
-#pragma unroll
-            for (int s = 0; s < kSteps; ++s)
-                acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(as_bf16x8(kf[blk][s]), qf[s], acc, 0, 0, 0);
-            sc[blk] = acc * c;
-        }
-        // mask the window's lower edge and the tail past p
-        const int base = jj * kPage;
-        if (base < rr.lo || base + kPage - 1 > rr.p) {
-#pragma unroll
-            for (int blk = 0; blk < 4; ++blk)
-#pragma unroll
-                for (int r = 0; r < 4; ++r) {
-                    const int kp = base + decode_key(blk, 4 * grp + r);
-                    if (kp < rr.lo || kp > rr.p) sc[blk][r] = -INFINITY;
-                }
-        }
-        float mx = sc[0][0];
-#pragma unroll
-        for (int blk = 0; blk < 4; ++blk)
-#pragma unroll
-            for (int r = 0; r < 4; ++r) mx = fmaxf(mx, sc[blk][r]);
-        mx = fmaxf(mx, __shfl_xor(mx, 16));
-        mx = fmaxf(mx, __shfl_xor(mx, 32));
-        const float m_new = fmaxf(m, mx);        // finite: every page holds a visible key
-        const float alpha = exp2f(m - m_new);
-        float ps = 0.f;
-#pragma unroll
-        for (int blk = 0; blk < 4; ++blk)
-#pragma unroll
-            for (int r = 0; r < 4; ++r) {
-                const float e = exp2f(sc[blk][r] - m_new);
-                sc[blk][r] = e;
-                ps += e;
-            }
-        lsum = lsum * alpha + ps;
-        m = m_new;
-#pragma unroll
-        for (int db = 0; db < kDimBlocks; ++db) o[db] *= alpha;
-
-        // O^T += V^T P^T, 32 keys per step
-#pragma unroll
-        for (int t = 0; t < 2; ++t) {
-            bf16x8 pf;
-#pragma unroll
-            for (int r = 0; r < 4; ++r) {
-                pf[r] = (__bf16)sc[2 * t][r];
-                pf[4 + r] = (__bf16)sc[2 * t + 1][r];
-            }
-#pragma unroll
-            for (int db = 0; db < kDimBlocks; ++db)
-                o[db] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(as_bf16x8(vf[t][db]), pf, o[db], 0, 0, 0);
-        }
+    // units u = 2*page + half of this chunk; wave w takes u = w, w+4, ...
+    // A unit is skipped if it lies past the chunk, its page id was bad, or
+    // none of its keys is in [lo, p]. The next unit's fragments load while
+    // the current one computes; the load is issued even for a skipped unit
+    // (from the pool's first tile, always in bounds) so that the number of
+    // loads in flight is the same on every path and the wait before the
+    // compute covers only the current unit.
+    const int n_units = 2 * n_local;
+    auto prep = [&](int u, int& base, const uint16_t*& kt, const uint16_t*& vt, int& half) -> bool {
+        kt = a.k_pool;
+        vt = a.v_pool;
+        half = 0;
+        if (u >= n_units) return false;
+        const int pg = s_pg[u >> 1];
+        base = (j0 + (u >> 1)) * kPage + 32 * (u & 1);
+        if (pg < 0 || base > rr.p || base + 31 < rr.lo) return false;
+        kt = a.k_pool + ((long long)pg * a.n_kv_heads + kh) * (kPage * D);
+        vt = a.v_pool + ((long long)pg * a.n_kv_heads + kh) * (kPage * D);
+        half = u & 1;
+        return true;
+    };
+    UnitFrags<D> fa, fb;
+    int base_a = 0, base_b = 0, half;
+    const uint16_t *kt, *vt;
+    int u = wave;
+    bool ok_a = prep(u, base_a, kt, vt, half);
+    load_unit<D>(fa, kt, vt, half, col, grp);
+    while (u < n_units) {
+        const bool ok_b = prep(u + kDecodeWaves, base_b, kt, vt, half);
+        load_unit<D>(fb, kt, vt, half, col, grp);
+        if (ok_a) compute_unit<D>(st, fa, qf, c, base_a, rr.lo, rr.p, grp);
+        u += kDecodeWaves;
+        if (u >= n_units) break;
+        ok_a = prep(u + kDecodeWaves, base_a, kt, vt, half);
+        load_unit<D>(fa, kt, vt, half, col, grp);
+        if (ok_b) compute_unit<D>(st, fb, qf, c, base_b, rr.lo, rr.p, grp);
+        u += kDecodeWaves;
     }
+    float m = st.m, lsum = st.lsum;
+    f32x4* o = st.o;
 
     // combine the four lane groups' partial sums (same column = same head)
     lsum += __shfl_xor(lsum, 16);
@@ -213,7 +256,8 @@ __global__ __launch_bounds__(kDecodeThreads, 2) void decode_kernel(AttnArgs a, i
 #pragma unroll
     for (int db = 0; db < kDimBlocks; ++db)
 #pragma unroll
-        for (int r = 0; r < 4; ++r) s_o[wave][16 * db + 4 * grp + r][col] = o[db][r];
+        for (int r = 0; r < 4; ++r)
+            if (col < G) s_o[(wave * D + 16 * db + 4 * grp + r) * G + col] = o[db][r];
     __syncthreads();
 
     // merge the waves: this chunk's (m, l, o) for each real head
@@ -230,7 +274,7 @@ __global__ __launch_bounds__(kDecodeThreads, 2) void decode_kernel(AttnArgs a, i
 #pragma unroll
             for (int w = 0; w < kDecodeWaves; ++w) {
                 const float sw = exp2f(s_m[w][j] - M);
-                ov += sw * s_o[w][d][j];
+                ov += sw * s_o[(w * D + d) * G + j];
                 lv += sw * s_l[w][j];
             }
         }
@@ -246,32 +290,39 @@ __global__ __launch_bounds__(kDecodeThreads, 2) void decode_kernel(AttnArgs a, i
             dst[D + 1] = lv;
         }
     }
-    if (n_splits == 1) return;
+}
 
-    // The last chunk to finish for this (row, kv head) merges all chunks:
-    // M = max m_s, out = sum_s 2^(m_s - M) o_s / sum_s 2^(m_s - M) l_s.
-    __shared__ int s_last;
-    __threadfence();                       // publish this chunk's partial device-wide
-    __syncthreads();
-    int* counter = reinterpret_cast<int*>(ws_counters) + pair;
-    if (tid == 0) s_last = atomicAdd(counter, 1) == n_splits - 1;
-    __syncthreads();
-    if (!s_last) return;
-    __threadfence();                       // see every other chunk's partial
-    if (tid == 0) *counter = 0;            // leave the counter zeroed for the next call
-    for (int item = tid; item < G * D; item += kDecodeThreads) {
+// Merge kernel: one workgroup per (row, kv head) whose range spans several
+// chunks: M = max m_s, out = sum_s 2^(m_s - M) o_s / sum_s 2^(m_s - M) l_s.
+// (Rows that fit one chunk were finished by the decode kernel.) Running it
+// as its own launch makes the chunks' partials visible without a device-wide
+// fence in every workgroup, which on a multi-XCD part writes back and
+// invalidates the whole L2.
+template <int D>
+__global__ __launch_bounds__(kDecodeThreads) void decode_merge_kernel(AttnArgs a, int pps, int max_splits,
+                                                                      const float* __restrict__ ws) {
+    const int kh = blockIdx.x;
+    const int b = blockIdx.y;
+    const RowRange rr = row_range(a, b, false);
+    if (!rr.ok) return;
+    const int n_splits = (rr.n_pg + pps - 1) / pps;
+    if (n_splits == 1) return;
+    const int G = a.n_q_heads / a.n_kv_heads;
+    const long long pair = (long long)b * a.n_kv_heads + kh;
+    const float* part = ws + pair * G * (long long)max_splits * (D + 2);
+    for (int item = threadIdx.x; item < G * D; item += kDecodeThreads) {
         const int j = item / D;
         const int d = item % D;
         const float* src = part + (long long)j * max_splits * (D + 2);
         float M = -INFINITY;
-        for (int sp = 0; sp < n_splits; ++sp) M = fmaxf(M, __builtin_nontemporal_load(src + sp * (D + 2) + D));
+        for (int sp = 0; sp < n_splits; ++sp) M = fmaxf(M, src[sp * (D + 2) + D]);
         float ov = 0.f, lv = 0.f;
         if (M != -INFINITY) {
             for (int sp = 0; sp < n_splits; ++sp) {
                 const float* e = src + sp * (D + 2);
-                const float w = exp2f(__builtin_nontemporal_load(e + D) - M);
-                ov += w * __builtin_nontemporal_load(e + d);
-                lv += w * __builtin_nontemporal_load(e + D + 1);
+                const float w = exp2f(e[D] - M);
+                ov += w * e[d];
+                lv += w * e[D + 1];
             }
         }
         a.out[(long long)b * a.ld_out + (long long)(kh * G + j) * D + d] =
@@ -292,37 +343,40 @@ DecodePlan decode_plan(int n_rows, int n_q_heads, int n_kv_heads, int head_dim, 
     long long pps = (pairs * max_pages + 8191) / 8192;
     pps = (pps + kDecodeWaves - 1) / kDecodeWaves * kDecodeWaves;
     if (pps < kDecodeWaves) pps = kDecodeWaves;
+    if (pps > kMaxPagesPerSplit) pps = kMaxPagesPerSplit;
     p.pages_per_split = (int)pps;
     p.max_splits = (int)((max_pages + pps - 1) / pps);
-    // one counter per (row, kv head) for the largest row count a call may
-    // have, at a fixed place: calls with different row counts share a
-    // workspace without their partials ever landing on counters
-    p.counter_bytes = ((size_t)kMaxDecodeRows * n_kv_heads * sizeof(int) + 255) / 256 * 256;
-    p.workspace_bytes = p.counter_bytes + (size_t)n_rows * n_q_heads * p.max_splits * (head_dim + 2) * sizeof(float);
+    p.workspace_bytes = (size_t)n_rows * n_q_heads * p.max_splits * (head_dim + 2) * sizeof(float);
     return p;
 }
 
 hipError_t launch_decode(const AttnArgs& a, const DecodePlan& plan, void* workspace, hipStream_t s,
                          Profiler* prof) {
     if (a.n_tokens <= 0) return hipSuccess;
-    int* counters = static_cast<int*>(workspace);
-    float* ws = reinterpret_cast<float*>(static_cast<char*>(workspace) + plan.counter_bytes);
+    float* ws = static_cast<float*>(workspace);
     dim3 grid(plan.max_splits, a.n_kv_heads, a.n_tokens), block(kDecodeThreads);
-    if (prof) prof->begin(DAP_KERNEL_DECODE, s);
+    dim3 mgrid(a.n_kv_heads, a.n_tokens);
+    const size_t lds = (size_t)kDecodeWaves * a.head_dim * (a.n_q_heads / a.n_kv_heads) * sizeof(float);
+    const int pps = plan.pages_per_split, ms = plan.max_splits;
+#define DAP_DECODE_CASE(DD)                                                                             \
+    case DD:                                                                                            \
+        if (prof) prof->begin(DAP_KERNEL_DECODE, s);                                                    \
+        hipLaunchKernelGGL(decode_kernel<DD>, grid, block, lds, s, a, pps, ms, ws);                     \
+        if (prof) prof->end(DAP_KERNEL_DECODE, s);                                                      \
+        if (ms > 1) {                                                                                   \
+            if (prof) prof->begin(DAP_KERNEL_DECODE_MERGE, s);                                          \
+            hipLaunchKernelGGL(decode_merge_kernel<DD>, mgrid, dim3(kDecodeThreads), 0, s, a, pps, ms, ws); \
+            if (prof) prof->end(DAP_KERNEL_DECODE_MERGE, s);                                            \
+        }                                                                                               \
+        break;
     switch (a.head_dim) {
-        case 64:
-            hipLaunchKernelGGL(decode_kernel<64>, grid, block, 0, s, a, plan.pages_per_split, plan.max_splits, ws, counters);
-            break;
-        case 96:
-            hipLaunchKernelGGL(decode_kernel<96>, grid, block, 0, s, a, plan.pages_per_split, plan.max_splits, ws, counters);
-            break;
-        case 128:
-            hipLaunchKernelGGL(decode_kernel<128>, grid, block, 0, s, a, plan.pages_per_split, plan.max_splits, ws, counters);
-            break;
+        DAP_DECODE_CASE(64)
+        DAP_DECODE_CASE(96)
+        DAP_DECODE_CASE(128)
         default:
             return hipErrorInvalidValue;
     }
-    if (prof) prof->end(DAP_KERNEL_DECODE, s);
+#undef DAP_DECODE_CASE
     return hipGetLastError();
 }
 

@@ -165,16 +165,12 @@ int dap_attn_prefill_packed(dap_handle* handle,
  * Row b (table row rows ? rows[b] : b, position p = positions[b]): the same
  * formula as the prefill for its one token. Keys are split into chunks of
  * pages processed in parallel; each chunk keeps a float32 running max,
- * sum and weighted V sum, and the last chunk of each (row, kv head) to
- * finish merges them exactly (max-shifted rescale) and rounds to bf16, all
- * in one kernel launch.
+ * sum and weighted V sum; a row that fits one chunk is finished in the
+ * same kernel, the others by a small second kernel that merges the chunks
+ * exactly (max-shifted rescale) and rounds to bf16.
  * q : [n_rows][ld_q] bf16 (roped), out : [n_rows][ld_out] bf16.
- * workspace : at least dap_decode_workspace_bytes(handle, n_rows) bytes,
- *             zero-filled before its first use. It starts with a fixed-size
- *             area of per-(row, kv head) counters that every completed call
- *             returns to zero, so one workspace serves all later calls of
- *             any row count up to the one it was sized for, one call at a
- *             time. n_rows is at most 65535.
+ * workspace : at least dap_decode_workspace_bytes(handle, n_rows) bytes of
+ *             scratch (any contents; one call at a time). n_rows <= 65535.
  */
 size_t dap_decode_workspace_bytes(const dap_handle* handle, int32_t n_rows);
 int dap_attn_decode_paged(dap_handle* handle,
@@ -198,8 +194,7 @@ int dap_attn_decode_paged(dap_handle* handle,
  * Runs the write over all tokens, then the packed prefill on the prompt
  * tokens and the decode on the step tokens, reading q from q_out.
  * out : [n_prompt + n_step][ld_out] bf16.
- * workspace : at least dap_step_workspace_bytes() bytes, zero-filled before
- *             its first use (it holds the decode workspace).
+ * workspace : at least dap_step_workspace_bytes() bytes of scratch.
  */
 size_t dap_step_workspace_bytes(const dap_handle* handle, int32_t n_prompt, int32_t n_segments,
                                 int32_t n_step);
@@ -229,7 +224,8 @@ enum {
     DAP_KERNEL_PREFILL_TILES = 1,  /* the prefill's tile-list pass */
     DAP_KERNEL_PREFILL = 2,        /* the prefill's attention kernel */
     DAP_KERNEL_DECODE = 3,         /* the decode kernel */
-    DAP_N_KERNELS = 4
+    DAP_KERNEL_DECODE_MERGE = 4,   /* the decode's cross-chunk merge */
+    DAP_N_KERNELS = 5
 };
 int dap_set_profiling(dap_handle* handle, int on);
 int dap_profile_read(dap_handle* handle, double* total_ms, int64_t* launches, int reset);

@@ -207,8 +207,8 @@ def test_inv_freq_table_matches_oracle():
 
 
 def test_decode_workspace_reused_across_row_counts():
-    """One zeroed workspace serves calls with different row counts: each
-    call must match a call on a fresh workspace bit for bit."""
+    """One workspace serves calls with different row counts: each call must
+    match a call on a fresh workspace bit for bit."""
     model = _model(32, 32, 96, 2047, max_position=4096)
     wl = _workload(model, 4, 64, "dec-ws-reuse")
     kp, vp = device_pools(wl)
@@ -226,6 +226,3 @@ def test_decode_workspace_reused_across_row_counts():
     torch.cuda.synchronize()
     for a, b, _, _ in keep:
         assert torch.equal(a.view(torch.int16), b.view(torch.int16))
-    # and the shared workspace's counters are all zero again
-    counters = ws[: 65535 * model.n_kv_heads * 4].view(torch.int32)
-    assert int(counters.abs().sum()) == 0
