@@ -328,6 +328,8 @@ int do_decode(dap_handle* h, const uint16_t* q, int64_t ld_q, int32_t n_rows, co
                                                   h->m.window, h->m.max_position);
     DAP_REQUIRE(workspace && workspace_bytes >= plan.workspace_bytes && aligned16(workspace), DAP_WORKSPACE_TOO_SMALL,
                 "workspace must be 16-byte aligned and at least dap_decode_workspace_bytes()");
+    DAP_REQUIRE((long long)plan.max_splits * h->m.n_kv_heads * n_rows < (1ll << 31), DAP_UNSUPPORTED,
+                "too many decode workgroups for one launch");
     if (h->validate) {
         std::vector<int32_t> hp, hr, ht;
         if (!to_host(hp, positions, n_rows, s) || (rows && !to_host(hr, rows, n_rows, s)) ||
@@ -363,6 +365,7 @@ int dap_create(const dap_model* mp, dap_handle** out) {
     DAP_REQUIRE(m.page_size == dap::kPage, DAP_UNSUPPORTED, "page_size must be 64");
     DAP_REQUIRE(m.window >= 0, DAP_INVALID_ARG, "window must be >= 0 (0 = none)");
     DAP_REQUIRE(m.max_position > 0, DAP_INVALID_ARG, "max_position must be positive");
+    DAP_REQUIRE(m.max_position <= (1 << 22), DAP_UNSUPPORTED, "max_position must be at most 4194304");
     DAP_REQUIRE(m.rope_theta > 0 && std::isfinite(m.rope_theta), DAP_INVALID_ARG, "rope_theta must be positive");
     if (m.llama3) {
         DAP_REQUIRE(m.llama3_factor > 0 && m.llama3_low_freq_factor > 0 &&

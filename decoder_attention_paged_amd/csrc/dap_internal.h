@@ -129,7 +129,8 @@ struct AttnArgs {
 };
 
 // Decode: split count and workspace layout.
-// Workspace: partials [n_rows][Hq][max_splits][D + 2] floats (o[D], m, l).
+// Workspace: partial o [n_rows][Hkv][max_splits][g][D] floats, then
+// (m, l) [n_rows][Hkv][max_splits][g][2] floats.
 struct DecodePlan {
     int pages_per_split;
     int max_splits;

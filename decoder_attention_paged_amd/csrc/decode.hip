@@ -39,6 +39,7 @@ __device__ __forceinline__ bf16x8 as_bf16x8(u32x4 u) { return __builtin_bit_cast
 __device__ __forceinline__ int unit_key(int blk, int i) { return 8 * (i >> 2) + 4 * blk + (i & 3); }
 
 constexpr int kMaxPagesPerSplit = 256;
+constexpr int kMaxSplits = 256;          // chunks per row (pps >= 4 caps this for max_position <= 65536)
 
 template <int D>
 struct UnitFrags {
@@ -46,18 +47,26 @@ struct UnitFrags {
     u32x4 v[D / 16];      // V^T, 16 dims x 32 keys per block
 };
 
+// Per-lane element offsets inside a page tile, fixed for the whole kernel:
+// K rows of the two 16-key blocks at dims 8*grp + 32s, V^T rows 16db + col.
+template <int D>
+struct LaneOffsets {
+    int k[2];    // + 32 * half * D selects the half page
+    int v;       // + 32 * half, + 16 * db * kPage per dim block
+};
+
 template <int D>
 __device__ __forceinline__ void load_unit(UnitFrags<D>& f, const uint16_t* kt, const uint16_t* vt, int half,
-                                          int col, int grp) {
+                                          const LaneOffsets<D>& lo) {
 #pragma unroll
     for (int blk = 0; blk < 2; ++blk) {
-        const uint16_t* kr = kt + (32 * half + unit_key(blk, col)) * D + 8 * grp;
+        const uint16_t* kr = kt + lo.k[blk] + 32 * half * D;
 #pragma unroll
         for (int s = 0; s < D / 32; ++s) f.k[blk][s] = *reinterpret_cast<const u32x4*>(kr + 32 * s);
     }
+    const uint16_t* vr = vt + lo.v + 32 * half;
 #pragma unroll
-    for (int db = 0; db < D / 16; ++db)
-        f.v[db] = *reinterpret_cast<const u32x4*>(vt + (16 * db + col) * kPage + 32 * half + 8 * grp);
+    for (int db = 0; db < D / 16; ++db) f.v[db] = *reinterpret_cast<const u32x4*>(vr + 16 * db * kPage);
 }
 
 struct RowRange {
@@ -99,6 +108,8 @@ struct WaveState {
 };
 
 // One 32-key unit: S = K q^T, mask, online softmax, O^T += V^T P^T.
+// Running max m is kept in scaled log2 units (scale folded into one FMA);
+// O is rescaled only when some head's max moved in this unit.
 template <int D>
 __device__ __forceinline__ void compute_unit(WaveState<D>& st, const UnitFrags<D>& f, const bf16x8* qf, float c,
                                              int base, int lo, int p, int grp) {
@@ -109,7 +120,7 @@ __device__ __forceinline__ void compute_unit(WaveState<D>& st, const UnitFrags<D
 #pragma unroll
         for (int s = 0; s < D / 32; ++s)
             acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(as_bf16x8(f.k[blk][s]), qf[s], acc, 0, 0, 0);
-        sc[blk] = acc * c;
+        sc[blk] = acc;
     }
     if (base < lo || base + 31 > p) {
 #pragma unroll
@@ -124,25 +135,28 @@ __device__ __forceinline__ void compute_unit(WaveState<D>& st, const UnitFrags<D
                      fmaxf(fmaxf(sc[1][0], sc[1][1]), fmaxf(sc[1][2], sc[1][3])));
     mx = fmaxf(mx, __shfl_xor(mx, 16));
     mx = fmaxf(mx, __shfl_xor(mx, 32));
-    const float m_new = fmaxf(st.m, mx);      // finite: every unit computed holds a visible key
-    const float alpha = exp2f(st.m - m_new);
+    const float m_new = fmaxf(st.m, mx * c);  // finite: every unit computed holds a visible key
+    if (__any(m_new > st.m)) {
+        const float alpha = __builtin_amdgcn_exp2f(st.m - m_new);
+        st.lsum *= alpha;
+#pragma unroll
+        for (int db = 0; db < D / 16; ++db) st.o[db] *= alpha;
+        st.m = m_new;
+    }
     float ps = 0.f;
     bf16x8 pf;
 #pragma unroll
     for (int blk = 0; blk < 2; ++blk)
 #pragma unroll
         for (int r = 0; r < 4; ++r) {
-            const float e = exp2f(sc[blk][r] - m_new);
+            const float e = __builtin_amdgcn_exp2f(__builtin_fmaf(sc[blk][r], c, -st.m));
             ps += e;
             pf[4 * blk + r] = (__bf16)e;
         }
-    st.lsum = st.lsum * alpha + ps;
-    st.m = m_new;
+    st.lsum += ps;
 #pragma unroll
-    for (int db = 0; db < D / 16; ++db) {
-        st.o[db] *= alpha;
+    for (int db = 0; db < D / 16; ++db)
         st.o[db] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(as_bf16x8(f.v[db]), pf, st.o[db], 0, 0, 0);
-    }
 }
 
 template <int D>
@@ -158,9 +172,15 @@ __global__ __launch_bounds__(kDecodeThreads, 2) void decode_kernel(AttnArgs a, i
     // heads only (sized at launch: 4 * D * g floats)
     extern __shared__ float s_o[];
 
-    const int split = blockIdx.x;
-    const int kh = blockIdx.y;
-    const int b = blockIdx.z;
+    // Workgroup order: kv head fastest (consecutive workgroups go to
+    // different XCDs, so each XCD gets the same share of every kv head),
+    // then row, then chunk index. Chunks are counted from the end of the row:
+    // chunk 0 is always a full chunk of pps pages and a row's partial chunk
+    // has its highest index, so the dispatcher starts full chunks first and
+    // the last workgroups it hands out are mostly partial ones.
+    const int kh = blockIdx.x % a.n_kv_heads;
+    const int b = (blockIdx.x / a.n_kv_heads) % a.n_tokens;
+    const int split = blockIdx.x / (a.n_kv_heads * a.n_tokens);
     const int tid = threadIdx.x;
     const int wave = tid >> 6;
     const int lane = tid & 63;
@@ -171,8 +191,9 @@ __global__ __launch_bounds__(kDecodeThreads, 2) void decode_kernel(AttnArgs a, i
     if (!rr.ok) return;
     const int n_splits = (rr.n_pg + pps - 1) / pps;
     if (split >= n_splits) return;
-    const int j0 = rr.first_pg + split * pps;
-    const int n_local = min(pps, rr.first_pg + rr.n_pg - j0);
+    const int j_hi = rr.first_pg + rr.n_pg - 1 - split * pps;      // last page of this chunk
+    const int j0 = max(rr.first_pg, j_hi - pps + 1);
+    const int n_local = j_hi - j0 + 1;
     const int G = a.n_q_heads / a.n_kv_heads;
 
     // this chunk's page ids, once, into LDS (-1 marks an out-of-range id)
@@ -213,12 +234,16 @@ __global__ __launch_bounds__(kDecodeThreads, 2) void decode_kernel(AttnArgs a, i
     // loads in flight is the same on every path and the wait before the
     // compute covers only the current unit.
     const int n_units = 2 * n_local;
+    LaneOffsets<D> lofs;
+    lofs.k[0] = unit_key(0, col) * D + 8 * grp;
+    lofs.k[1] = unit_key(1, col) * D + 8 * grp;
+    lofs.v = col * kPage + 8 * grp;
     auto prep = [&](int u, int& base, const uint16_t*& kt, const uint16_t*& vt, int& half) -> bool {
         kt = a.k_pool;
         vt = a.v_pool;
         half = 0;
         if (u >= n_units) return false;
-        const int pg = s_pg[u >> 1];
+        const int pg = __builtin_amdgcn_readfirstlane(s_pg[u >> 1]);   // the same for the whole wave
         base = (j0 + (u >> 1)) * kPage + 32 * (u & 1);
         if (pg < 0 || base > rr.p || base + 31 < rr.lo) return false;
         kt = a.k_pool + ((long long)pg * a.n_kv_heads + kh) * (kPage * D);
@@ -231,15 +256,15 @@ __global__ __launch_bounds__(kDecodeThreads, 2) void decode_kernel(AttnArgs a, i
     const uint16_t *kt, *vt;
     int u = wave;
     bool ok_a = prep(u, base_a, kt, vt, half);
-    load_unit<D>(fa, kt, vt, half, col, grp);
+    load_unit<D>(fa, kt, vt, half, lofs);
     while (u < n_units) {
         const bool ok_b = prep(u + kDecodeWaves, base_b, kt, vt, half);
-        load_unit<D>(fb, kt, vt, half, col, grp);
+        load_unit<D>(fb, kt, vt, half, lofs);
         if (ok_a) compute_unit<D>(st, fa, qf, c, base_a, rr.lo, rr.p, grp);
         u += kDecodeWaves;
         if (u >= n_units) break;
         ok_a = prep(u + kDecodeWaves, base_a, kt, vt, half);
-        load_unit<D>(fa, kt, vt, half, col, grp);
+        load_unit<D>(fa, kt, vt, half, lofs);
         if (ok_b) compute_unit<D>(st, fb, qf, c, base_b, rr.lo, rr.p, grp);
         u += kDecodeWaves;
     }
@@ -262,7 +287,9 @@ __global__ __launch_bounds__(kDecodeThreads, 2) void decode_kernel(AttnArgs a, i
 
     // merge the waves: this chunk's (m, l, o) for each real head
     const long long pair = (long long)b * a.n_kv_heads + kh;
-    float* part = ws + pair * G * (long long)max_splits * (D + 2);   // [G][max_splits][D + 2]
+    const long long slot = pair * max_splits + split;
+    float* part_o = ws + slot * G * D;                                        // [G][D]
+    float* part_ml = ws + (long long)a.n_tokens * a.n_kv_heads * max_splits * G * D + slot * G * 2;
     for (int item = tid; item < G * D; item += kDecodeThreads) {
         const int j = item / D;
         const int d = item % D;
@@ -283,11 +310,10 @@ __global__ __launch_bounds__(kDecodeThreads, 2) void decode_kernel(AttnArgs a, i
                 (uint16_t)f32_to_bf16(lv > 0.f ? ov / lv : 0.f);
             continue;
         }
-        float* dst = part + ((long long)j * max_splits + split) * (D + 2);
-        dst[d] = ov;
+        part_o[item] = ov;
         if (d == 0) {
-            dst[D] = M;
-            dst[D + 1] = lv;
+            part_ml[2 * j] = M;
+            part_ml[2 * j + 1] = lv;
         }
     }
 }
@@ -301,32 +327,48 @@ __global__ __launch_bounds__(kDecodeThreads, 2) void decode_kernel(AttnArgs a, i
 template <int D>
 __global__ __launch_bounds__(kDecodeThreads) void decode_merge_kernel(AttnArgs a, int pps, int max_splits,
                                                                       const float* __restrict__ ws) {
+    __shared__ float s_w[kMaxSplits * 16];     // per (chunk, head): 2^(m_s - M)
+    __shared__ float s_inv_l[16];
     const int kh = blockIdx.x;
     const int b = blockIdx.y;
+    const int tid = threadIdx.x;
     const RowRange rr = row_range(a, b, false);
     if (!rr.ok) return;
     const int n_splits = (rr.n_pg + pps - 1) / pps;
     if (n_splits == 1) return;
     const int G = a.n_q_heads / a.n_kv_heads;
-    const long long pair = (long long)b * a.n_kv_heads + kh;
-    const float* part = ws + pair * G * (long long)max_splits * (D + 2);
-    for (int item = threadIdx.x; item < G * D; item += kDecodeThreads) {
-        const int j = item / D;
-        const int d = item % D;
-        const float* src = part + (long long)j * max_splits * (D + 2);
+    const long long slot0 = ((long long)b * a.n_kv_heads + kh) * max_splits;
+    const float* part_o = ws + slot0 * G * D;
+    const float* part_ml = ws + (long long)a.n_tokens * a.n_kv_heads * max_splits * G * D + slot0 * G * 2;
+    // every chunk's m in parallel, then per head the max, the weights and 1/L
+    for (int i = tid; i < n_splits * G; i += kDecodeThreads) s_w[i] = part_ml[2 * i];
+    __syncthreads();
+    if (tid < G) {
         float M = -INFINITY;
-        for (int sp = 0; sp < n_splits; ++sp) M = fmaxf(M, src[sp * (D + 2) + D]);
-        float ov = 0.f, lv = 0.f;
-        if (M != -INFINITY) {
-            for (int sp = 0; sp < n_splits; ++sp) {
-                const float* e = src + sp * (D + 2);
-                const float w = exp2f(e[D] - M);
-                ov += w * e[d];
-                lv += w * e[D + 1];
-            }
+        for (int sp = 0; sp < n_splits; ++sp) M = fmaxf(M, s_w[sp * G + tid]);
+        float L = 0.f;
+        for (int sp = 0; sp < n_splits; ++sp) {
+            const float w = M == -INFINITY ? 0.f : exp2f(s_w[sp * G + tid] - M);
+            s_w[sp * G + tid] = w;
+            L += w * part_ml[2 * (sp * G + tid) + 1];
         }
-        a.out[(long long)b * a.ld_out + (long long)(kh * G + j) * D + d] =
-            (uint16_t)f32_to_bf16(lv > 0.f ? ov / lv : 0.f);
+        s_inv_l[tid] = L > 0.f ? 1.f / L : 0.f;
+    }
+    __syncthreads();
+    for (int item = tid; item < G * D; item += kDecodeThreads) {
+        const int j = item / D;
+        const float* src = part_o + item;
+        float ov0 = 0.f, ov1 = 0.f, ov2 = 0.f, ov3 = 0.f;
+        int sp = 0;
+        for (; sp + 4 <= n_splits; sp += 4) {   // independent loads in flight together
+            ov0 += s_w[sp * G + j] * src[(long long)sp * G * D];
+            ov1 += s_w[(sp + 1) * G + j] * src[(long long)(sp + 1) * G * D];
+            ov2 += s_w[(sp + 2) * G + j] * src[(long long)(sp + 2) * G * D];
+            ov3 += s_w[(sp + 3) * G + j] * src[(long long)(sp + 3) * G * D];
+        }
+        for (; sp < n_splits; ++sp) ov0 += s_w[sp * G + j] * src[(long long)sp * G * D];
+        const float ov = (ov0 + ov1) + (ov2 + ov3);
+        a.out[(long long)b * a.ld_out + (long long)(kh * G) * D + item] = (uint16_t)f32_to_bf16(ov * s_inv_l[j]);
     }
 }
 
@@ -344,8 +386,10 @@ DecodePlan decode_plan(int n_rows, int n_q_heads, int n_kv_heads, int head_dim, 
     pps = (pps + kDecodeWaves - 1) / kDecodeWaves * kDecodeWaves;
     if (pps < kDecodeWaves) pps = kDecodeWaves;
     if (pps > kMaxPagesPerSplit) pps = kMaxPagesPerSplit;
+    if ((max_pages + pps - 1) / pps > kMaxSplits) pps = (max_pages + kMaxSplits - 1) / kMaxSplits;
     p.pages_per_split = (int)pps;
     p.max_splits = (int)((max_pages + pps - 1) / pps);
+    // partials: o [n_rows][Hkv][max_splits][g][D], then (m, l) [n_rows][Hkv][max_splits][g][2]
     p.workspace_bytes = (size_t)n_rows * n_q_heads * p.max_splits * (head_dim + 2) * sizeof(float);
     return p;
 }
@@ -354,7 +398,7 @@ hipError_t launch_decode(const AttnArgs& a, const DecodePlan& plan, void* worksp
                          Profiler* prof) {
     if (a.n_tokens <= 0) return hipSuccess;
     float* ws = static_cast<float*>(workspace);
-    dim3 grid(plan.max_splits, a.n_kv_heads, a.n_tokens), block(kDecodeThreads);
+    dim3 grid((unsigned)plan.max_splits * a.n_kv_heads * a.n_tokens), block(kDecodeThreads);
     dim3 mgrid(a.n_kv_heads, a.n_tokens);
     const size_t lds = (size_t)kDecodeWaves * a.head_dim * (a.n_q_heads / a.n_kv_heads) * sizeof(float);
     const int pps = plan.pages_per_split, ms = plan.max_splits;

@@ -62,7 +62,7 @@ typedef struct dap_model {
     int32_t head_dim;              /* D: 64, 96 or 128 */
     int32_t page_size;             /* must be 64 */
     int32_t window;                /* 0: none; W > 0: a query at p sees keys p-W < j <= p */
-    int32_t max_position;          /* positions lie in [0, max_position) */
+    int32_t max_position;          /* positions lie in [0, max_position), at most 4194304 */
     double rope_theta;             /* rotary base, > 0 */
     int32_t llama3;                /* nonzero: llama3 three-band frequency rescale */
     double llama3_factor;          /* e.g. 8 */
