@@ -205,12 +205,12 @@ def cpu_baseline(b: Bench, budget_s: float = 20.0):
     # the sample: every token's front half (write), a few prompts / decode rows
     if b.name == "qwen3":
         tok_pos, tok_rows = b.pos_np, b.rows_np
-        pre_pick = np.nonzero(np.isin(wl.pre_segments, [0, 4]))[0]
-        dec_pick = np.arange(8)
+        pre_pick = np.arange(wl.n_pre)
+        dec_pick = np.arange(wl.n_dec)
     elif b.name == "mistral":
         tok_pos, tok_rows = wl.dec_positions, wl.dec_rows
         pre_pick = np.zeros(0, int)
-        dec_pick = np.arange(8)
+        dec_pick = np.arange(wl.n_dec)
     else:
         tok_pos, tok_rows = wl.pre_positions, wl.pre_segments
         pre_pick = np.arange(0, wl.n_pre, max(1, wl.n_pre // (64 if b.name == "llama31" else 512)))
@@ -240,17 +240,14 @@ def cpu_baseline(b: Bench, budget_s: float = 20.0):
     written = {}
     for t, s in enumerate(slots):
         written.setdefault(int(s) // 64, []).append((int(s) % 64, t))
-    pages_f64 = {}
-
     def read_page(pg):
-        if pg not in pages_f64:
-            kk, vv = cache[pg]
+        kk, vv = cache[pg]
+        if pg in written:
             kk, vv = kk.copy(), vv.copy()
-            for i, t in written.get(pg, []):
+            for i, t in written[pg]:
                 kk[:, i] = k_bits[t]
                 vv[:, i] = vb[t]
-            pages_f64[pg] = (bf16.to_f64(kk), bf16.to_f64(vv))
-        return pages_f64[pg]
+        return bf16.to_f64(kk), bf16.to_f64(vv)
 
     qf = bf16.to_f64(q_bits)
     done_bytes = write_bytes(m, len(tok_pos))
@@ -286,7 +283,7 @@ def traffic_for(kernel: str, workload: str):
     digest = hashlib.sha256(open(src, "rb").read()).hexdigest()
     if digest != rec.get("source_sha256"):
         return None
-    return rec.get("bytes_per_launch")
+    return rec.get("bytes_per_launch", {}).get("total")
 
 
 def main():
