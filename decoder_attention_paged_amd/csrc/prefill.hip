@@ -8,13 +8,15 @@
 // position, which covers chunks and shared prefixes).
 //
 // A tile-list pass cuts the packed tokens into runs of equal segment id and
-// each run into tiles of at most 128/g tokens. One workgroup (4 waves) takes
+// each run into tiles of at most 256/g tokens. One workgroup (8 waves) takes
 // one (tile, kv head): wave w owns 32 query rows = one of the g query heads
 // sharing the kv head, for 32 of the tile's tokens, so each K/V page tile is
-// read from memory once per workgroup for all g heads. Per 64-key page the
-// workgroup stages K (slot-major) and V^T (dim-major) through LDS, and each
+// read from memory once per workgroup for all g heads and 256 query rows.
+// Per 64-key page the workgroup stages K (slot-major) and V^T (dim-major)
+// into one of two LDS buffers (one barrier per page), and each
 // wave computes S^T = K Q^T and O^T += V^T P^T with 32x32x16 bf16 MFMAs and
-// an online softmax in float32 (exp2 with the scale folded in). Pages fully
+// an online softmax in float32 (exp2 with the scale folded in, O rescaled
+// only when a row's running max moves). Pages fully
 // outside a wave's rows are skipped; only pages that straddle a row's causal
 // or window edge are masked element by element. Workgroups are numbered
 // kv-head-fastest so blocks sharing a kv head land on the same XCD (L2).
@@ -24,7 +26,8 @@ namespace dap {
 
 namespace {
 
-constexpr int kPrefillThreads = 256;   // 4 waves
+constexpr int kPrefillWaves = 8;
+constexpr int kPrefillThreads = 64 * kPrefillWaves;
 constexpr int kTilesThreads = 1024;
 constexpr float kLog2e = 1.4426950408889634f;
 constexpr unsigned kErrSegments = 32u;
@@ -111,17 +114,19 @@ __device__ __forceinline__ int wave_max(int v) {
 __device__ __forceinline__ int swap23(int i) { return (i & ~12) | ((i & 4) << 1) | ((i & 8) >> 1); }
 
 template <int D, int G>
-__global__ __launch_bounds__(kPrefillThreads, 2) void prefill_kernel(AttnArgs a, const int* __restrict__ tiles,
-                                                                     int cap) {
-    constexpr int BM = 128 / G;         // tokens per tile
+__global__ __launch_bounds__(kPrefillThreads) void prefill_kernel(AttnArgs a, const int* __restrict__ tiles,
+                                                                  int cap) {
+    constexpr int BM = 32 * kPrefillWaves / G;   // tokens per tile
     constexpr int KS = D + 8;           // LDS row stride of K (elements)
     constexpr int VS = kPage + 8;       // LDS row stride of V^T (elements)
     constexpr int kSteps = D / 16;      // QK k-steps
     constexpr int kDimBlocks = D / 32;  // PV output blocks
-    constexpr int kChunks = D / 32;     // 16-byte chunks per thread per tensor per page
+    constexpr int kTileChunks = 8 * D;  // 16-byte chunks per tensor per page
+    constexpr int kChunks = (kTileChunks + kPrefillThreads - 1) / kPrefillThreads;
+    constexpr int kBufElems = kPage * KS + D * VS;
 
-    __shared__ __attribute__((aligned(16))) uint16_t s_k[kPage * KS];
-    __shared__ __attribute__((aligned(16))) uint16_t s_v[D * VS];
+    // two page buffers (K then V^T in each), written and read alternately
+    extern __shared__ __attribute__((aligned(16))) uint16_t s_buf[];
 
     const int n_tiles = tiles[cap + 1];
     const int kh = blockIdx.x % a.n_kv_heads;
@@ -213,50 +218,76 @@ __global__ __launch_bounds__(kPrefillThreads, 2) void prefill_kernel(AttnArgs a,
 #pragma unroll
         for (int i = 0; i < kChunks; ++i) {
             const int cidx = tid + kPrefillThreads * i;
-            pk[i] = *reinterpret_cast<const u32x4*>(kt + 8 * cidx);
-            pv[i] = *reinterpret_cast<const u32x4*>(vt + 8 * cidx);
+            if (kTileChunks % kPrefillThreads == 0 || cidx < kTileChunks) {
+                pk[i] = *reinterpret_cast<const u32x4*>(kt + 8 * cidx);
+                pv[i] = *reinterpret_cast<const u32x4*>(vt + 8 * cidx);
+            }
         }
         return true;
     };
-    bool have = prefetch(j_first);
+    auto stage = [&](int buf) {
+        uint16_t* sk = s_buf + buf * kBufElems;
+        uint16_t* sv = sk + kPage * KS;
+#pragma unroll
+        for (int i = 0; i < kChunks; ++i) {
+            const int cidx = tid + kPrefillThreads * i;
+            if (kTileChunks % kPrefillThreads == 0 || cidx < kTileChunks) {
+                const int kr = cidx / (D / 8), kc = cidx % (D / 8);
+                *reinterpret_cast<u32x4*>(&sk[kr * KS + 8 * kc]) = pk[i];
+                const int vr = cidx / (kPage / 8), vc = cidx % (kPage / 8);
+                *reinterpret_cast<u32x4*>(&sv[vr * VS + 8 * vc]) = pv[i];
+            }
+        }
+    };
+
+    // Pipeline: page j computes from LDS buffer (j - j_first) & 1 while page
+    // j+1's tile, prefetched into registers during page j-1, is written to
+    // the other buffer; one barrier per page.
+    bool ok_next = prefetch(j_first);
+    if (ok_next) stage(0);
+    bool ok_cur = ok_next;
+    __syncthreads();
+    if (j_first < j_last) ok_next = prefetch(j_first + 1);
 
     for (int j = j_first; j <= j_last; ++j) {
-        __syncthreads();                       // everyone is done reading the previous tile
-        const bool cur = have;
-        if (cur) {
-#pragma unroll
-            for (int i = 0; i < kChunks; ++i) {
-                const int cidx = tid + kPrefillThreads * i;
-                const int kr = cidx / (D / 8), kc = cidx % (D / 8);
-                *reinterpret_cast<u32x4*>(&s_k[kr * KS + 8 * kc]) = pk[i];
-                const int vr = cidx / (kPage / 8), vc = cidx % (kPage / 8);
-                *reinterpret_cast<u32x4*>(&s_v[vr * VS + 8 * vc]) = pv[i];
-            }
-        } else if (tid == 0 && kh == 0) {
-            atomicOr(a.err, kErrPage);
-        }
-        __syncthreads();
-        if (j < j_last) have = prefetch(j + 1);
-        if (!cur) continue;
-
+        const int buf = (j - j_first) & 1;
+        const uint16_t* s_k = s_buf + buf * kBufElems;
+        const uint16_t* s_v = s_k + kPage * KS;
         const int k0 = j * kPage;
-        if (k0 > w_pmax || k0 + kPage - 1 < w_lomin) continue;    // nothing visible to this wave
-
-        // S^T = K Q^T : two 32-key blocks
+        if (!ok_cur && tid == 0 && kh == 0) atomicOr(a.err, kErrPage);
+        if (ok_cur && !(k0 > w_pmax || k0 + kPage - 1 < w_lomin)) {   // skip pages invisible to this wave
+        // S^T = K Q^T : two 32-key blocks. All K fragments are read from LDS
+        // first (they return in order, so the MFMAs then issue back to back);
+        // the scheduling barrier keeps the compiler from pairing each read
+        // with its MFMA, which would expose the LDS latency every time.
+        u32x4 kf[2][kSteps];
+#pragma unroll
+        for (int blk = 0; blk < 2; ++blk) {
+            const uint16_t* kr = &s_k[(32 * blk + swap23(row)) * KS + 8 * half];
+#pragma unroll
+            for (int s = 0; s < kSteps; ++s) kf[blk][s] = *reinterpret_cast<const u32x4*>(kr + 16 * s);
+        }
+        __builtin_amdgcn_sched_barrier(0);
         f32x16 sc[2];
 #pragma unroll
         for (int blk = 0; blk < 2; ++blk) {
             f32x16 acc;
 #pragma unroll
             for (int r = 0; r < 16; ++r) acc[r] = 0.f;
-            const uint16_t* kr = &s_k[(32 * blk + swap23(row)) * KS + 8 * half];
 #pragma unroll
-            for (int s = 0; s < kSteps; ++s) {
-                const u32x4 kf = *reinterpret_cast<const u32x4*>(kr + 16 * s);
-                acc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(as_bf16x8(kf), qf[s], acc, 0, 0, 0);
-            }
-            sc[blk] = acc * c;
+            for (int s = 0; s < kSteps; ++s)
+                acc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(as_bf16x8(kf[blk][s]), qf[s], acc, 0, 0, 0);
+            sc[blk] = acc;                     // unscaled; the scale folds into the exp2 argument
         }
+        // V^T fragments for the PV step, read now so their latency hides
+        // under the softmax below
+        u32x4 vfr[4][kDimBlocks];
+#pragma unroll
+        for (int t = 0; t < 4; ++t)
+#pragma unroll
+            for (int db = 0; db < kDimBlocks; ++db)
+                vfr[t][db] = *reinterpret_cast<const u32x4*>(&s_v[(32 * db + row) * VS + 16 * t + 8 * half]);
+        __builtin_amdgcn_sched_barrier(0);
         // mask where this page crosses an edge of some row's range
         if (k0 < w_lomax || k0 + kPage - 1 > w_pmin) {
 #pragma unroll
@@ -274,22 +305,27 @@ __global__ __launch_bounds__(kPrefillThreads, 2) void prefill_kernel(AttnArgs a,
 #pragma unroll
             for (int r = 0; r < 16; ++r) mx = fmaxf(mx, sc[blk][r]);
         mx = fmaxf(mx, __shfl_xor(mx, 32));
-        const float m_new = fmaxf(m, mx);
-        const float m_ref = m_new == -INFINITY ? 0.f : m_new;
-        const float alpha = exp2f(m - m_ref);
+        // running max in scaled log2 units; O and l are rescaled only when
+        // some row's max moved (rare once a row has seen a few pages)
+        const float m_new = fmaxf(m, mx * c);
+        if (__any(m_new > m)) {
+            const float alpha = m_new > m ? __builtin_amdgcn_exp2f(m - m_new) : 1.f;
+            lsum *= alpha;
+#pragma unroll
+            for (int db = 0; db < kDimBlocks; ++db) o[db] *= alpha;
+            m = m_new;
+        }
+        const float m_ref = m == -INFINITY ? 0.f : m;     // a row with nothing visible yet
         float ps = 0.f;
 #pragma unroll
         for (int blk = 0; blk < 2; ++blk)
 #pragma unroll
             for (int r = 0; r < 16; ++r) {
-                const float e = exp2f(sc[blk][r] - m_ref);
+                const float e = __builtin_amdgcn_exp2f(__builtin_fmaf(sc[blk][r], c, -m_ref));
                 sc[blk][r] = e;
                 ps += e;
             }
-        lsum = lsum * alpha + ps;
-        m = m_new;
-#pragma unroll
-        for (int db = 0; db < kDimBlocks; ++db) o[db] *= alpha;
+        lsum += ps;
 
         // O^T += V^T P^T : four 16-key steps
 #pragma unroll
@@ -298,11 +334,16 @@ __global__ __launch_bounds__(kPrefillThreads, 2) void prefill_kernel(AttnArgs a,
 #pragma unroll
             for (int e = 0; e < 8; ++e) pf[e] = (__bf16)sc[t >> 1][8 * (t & 1) + e];
 #pragma unroll
-            for (int db = 0; db < kDimBlocks; ++db) {
-                const u32x4 vf = *reinterpret_cast<const u32x4*>(&s_v[(32 * db + row) * VS + 16 * t + 8 * half]);
-                o[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(as_bf16x8(vf), pf, o[db], 0, 0, 0);
-            }
+            for (int db = 0; db < kDimBlocks; ++db)
+                o[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(as_bf16x8(vfr[t][db]), pf, o[db], 0, 0, 0);
         }
+        }
+        // next page into the other buffer (its previous contents were last read
+        // before the previous barrier), then one barrier
+        if (j < j_last && ok_next) stage(buf ^ 1);
+        ok_cur = ok_next;
+        __syncthreads();
+        if (j + 1 < j_last) ok_next = prefetch(j + 2);
     }
 
     lsum += __shfl_xor(lsum, 32);
@@ -319,20 +360,33 @@ __global__ __launch_bounds__(kPrefillThreads, 2) void prefill_kernel(AttnArgs a,
         }
 }
 
-template <int D>
-hipError_t launch_prefill_d(const AttnArgs& a, int G, int cap, const int* tiles, hipStream_t s) {
-    dim3 grid((unsigned)cap * a.n_kv_heads), block(kPrefillThreads);
-    switch (G) {
-        case 1: hipLaunchKernelGGL((prefill_kernel<D, 1>), grid, block, 0, s, a, tiles, cap); break;
-        case 2: hipLaunchKernelGGL((prefill_kernel<D, 2>), grid, block, 0, s, a, tiles, cap); break;
-        case 4: hipLaunchKernelGGL((prefill_kernel<D, 4>), grid, block, 0, s, a, tiles, cap); break;
-        default: return hipErrorInvalidValue;
+template <int D, int G>
+hipError_t launch_prefill_dg(const AttnArgs& a, int cap, const int* tiles, hipStream_t s) {
+    constexpr size_t lds = 2 * (kPage * (D + 8) + D * (kPage + 8)) * sizeof(uint16_t);
+    static bool configured = false;     // raise the dynamic LDS limit once per instantiation
+    if (!configured) {
+        hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void*>(&prefill_kernel<D, G>),
+                                           hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds);
+        if (e != hipSuccess) return e;
+        configured = true;
     }
+    hipLaunchKernelGGL((prefill_kernel<D, G>), dim3((unsigned)cap * a.n_kv_heads), dim3(kPrefillThreads), lds, s, a,
+                       tiles, cap);
     return hipGetLastError();
 }
 
+template <int D>
+hipError_t launch_prefill_d(const AttnArgs& a, int G, int cap, const int* tiles, hipStream_t s) {
+    switch (G) {
+        case 1: return launch_prefill_dg<D, 1>(a, cap, tiles, s);
+        case 2: return launch_prefill_dg<D, 2>(a, cap, tiles, s);
+        case 4: return launch_prefill_dg<D, 4>(a, cap, tiles, s);
+        default: return hipErrorInvalidValue;
+    }
+}
+
 int tile_cap(int n_tokens, int n_segments, int group) {
-    const int bm = 128 / group;
+    const int bm = 32 * kPrefillWaves / group;
     return (n_tokens + bm - 1) / bm + n_segments;
 }
 
@@ -348,8 +402,8 @@ hipError_t launch_prefill(const AttnArgs& a, int n_segments, void* workspace, hi
     const int cap = tile_cap(a.n_tokens, n_segments, G);
     int* tiles = static_cast<int*>(workspace);
     if (prof) prof->begin(DAP_KERNEL_PREFILL_TILES, s);
-    hipLaunchKernelGGL(prefill_tiles_kernel, dim3(1), dim3(kTilesThreads), 0, s, a.rows, a.n_tokens, 128 / G, cap,
-                       tiles, a.err);
+    hipLaunchKernelGGL(prefill_tiles_kernel, dim3(1), dim3(kTilesThreads), 0, s, a.rows, a.n_tokens,
+                       32 * kPrefillWaves / G, cap, tiles, a.err);
     if (prof) prof->end(DAP_KERNEL_PREFILL_TILES, s);
     hipError_t e = hipGetLastError();
     if (e != hipSuccess) return e;
