@@ -268,6 +268,26 @@ def cpu_baseline(b: Bench, budget_s: float = 20.0):
             "sample": sample, "seconds": round(dt, 2)}
 
 
+# --------------------------------------------------------------------------- copy ceiling
+def copy_ceiling(nbytes: int = 1 << 30, reps: int = 10) -> float:
+    """Measured device-to-device copy rate (bytes read + bytes written per
+    second, GB/s): the practical HBM ceiling beside the vendor figure."""
+    x = torch.empty(nbytes, dtype=torch.uint8, device="cuda")
+    y = torch.empty_like(x)
+    y.copy_(x)
+    a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    torch.cuda.synchronize()
+    a.record()
+    for _ in range(reps):
+        y.copy_(x)
+    b.record()
+    torch.cuda.synchronize()
+    gbps = 2 * nbytes * reps / (a.elapsed_time(b) * 1e-3) / 1e9
+    del x, y
+    torch.cuda.empty_cache()
+    return round(gbps, 1)
+
+
 # --------------------------------------------------------------------------- traffic counters
 def traffic_for(kernel: str, workload: str):
     """HBM bytes per launch from the committed rocprofv3 counter summary,
@@ -319,15 +339,20 @@ def main():
     wall = time.perf_counter() - t0
     ms_per_step = wall * 1e3 / args.steps
 
-    # second timed pass with the library's per-launch events
+    # second timed pass with the library's per-launch events, plus one stream
+    # event per step for the spread of step times
     b.h.set_profiling(True)
     b.h.profile_read(reset=True)
-    for _ in range(args.steps):
+    marks = [torch.cuda.Event(enable_timing=True) for _ in range(args.steps + 1)]
+    marks[0].record()
+    for i in range(args.steps):
         b.step()
+        marks[i + 1].record()
     torch.cuda.synchronize()
     prof = b.h.profile_read(reset=True)
     b.h.set_profiling(False)
     kern_ms = {k: (v[0] / v[1] if v[1] else 0.0) for k, v in prof.items()}
+    step_ms = np.array([marks[i].elapsed_time(marks[i + 1]) for i in range(args.steps)])
 
     m = b.m
     value = b.bytes / (ms_per_step * 1e-3) / 1e9
@@ -360,6 +385,9 @@ def main():
         "event_ms_per_step": round(start.elapsed_time(stop) / args.steps, 4),
         "tokens_per_s": round(b.tokens / (ms_per_step * 1e-3), 1),
         "kernel_avg_ms": {k: round(v, 5) for k, v in kern_ms.items() if prof[k][1]},
+        "step_ms_median": round(float(np.median(step_ms)), 4),
+        "step_ms_spread": [round(float(step_ms.min()), 4), round(float(step_ms.max()), 4)],
+        "hbm_copy_ceiling_gbps": copy_ceiling(),
     }
     if b.flops:
         line["prefill_tflops"] = round(b.flops / (kern_ms["prefill"] * 1e-3) / 1e12, 2)
