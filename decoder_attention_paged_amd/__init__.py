@@ -26,9 +26,11 @@ OK, INVALID_ARG, UNSUPPORTED, WORKSPACE_TOO_SMALL, HIP_ERROR, BAD_INDEX = 0, -1,
 EXPORTS = ("dap_create", "dap_destroy", "dap_last_error", "dap_set_validate", "dap_inv_freq",
            "dap_rope_qknorm_write_pages", "dap_prefill_workspace_bytes", "dap_attn_prefill_packed",
            "dap_decode_workspace_bytes", "dap_attn_decode_paged", "dap_step_workspace_bytes",
-           "dap_step_paged", "dap_set_profiling", "dap_profile_read")
+           "dap_step_paged", "dap_set_profiling", "dap_profile_read", "dap_cache_workspace_bytes",
+           "dap_decode", "dap_decode_rows", "dap_prefill", "dap_prefill_slots", "dap_inpass_workspace_bytes",
+           "dap_packed", "dap_forward")
 
-KERNELS = ("write", "prefill_tiles", "prefill", "decode", "decode_merge")
+KERNELS = ("write", "prefill_tiles", "prefill", "decode", "decode_merge", "prep")
 
 
 class DapError(RuntimeError):
@@ -88,6 +90,18 @@ def load_library(path: str = LIB_PATH):
     lib.dap_step_paged.argtypes = [
         _P, _P, _P, _P, _I64, _I32, _I32, _I32, _P, _P, _P, _P, _I32, _I32, _P, _P, _P, _I64,
         _P, _P, _I32, _P, _I64, _P, _SZ, _P]
+    lib.dap_cache_workspace_bytes.argtypes = [_P, _I32, _I32, _I32, _I32]
+    lib.dap_cache_workspace_bytes.restype = _SZ
+    lib.dap_decode.argtypes = [_P, _P, _P, _P, _I64, _I32, _I32, _I32, _P, _P, _P, _P, _P, _I64, _P, _SZ, _P]
+    lib.dap_decode_rows.argtypes = [_P, _P, _P, _P, _I64, _I32, _P, _I32, _P, _P, _P, _P, _P, _I64, _P, _SZ, _P]
+    lib.dap_prefill.argtypes = [_P, _P, _P, _P, _I64, _I32, _I32, _I32, _I32, _P, _P, _P, _P, _P, _I64, _P, _SZ,
+                                _P]
+    lib.dap_prefill_slots.argtypes = [_P, _P, _P, _P, _I64, _I32, _I32, _P, _I32, _I32, _P, _P, _P, _P, _P, _I64,
+                                      _P, _SZ, _P]
+    lib.dap_inpass_workspace_bytes.argtypes = [_P, _I32, _I32]
+    lib.dap_inpass_workspace_bytes.restype = _SZ
+    lib.dap_packed.argtypes = [_P, _P, _P, _P, _I64, _I32, _P, _P, _I32, _P, _P, _P, _I64, _P, _SZ, _P]
+    lib.dap_forward.argtypes = [_P, _P, _P, _P, _I64, _I32, _I32, _P, _P, _P, _I64, _P, _SZ, _P]
     lib.dap_set_profiling.argtypes = [_P, ctypes.c_int]
     lib.dap_profile_read.argtypes = [_P, ctypes.POINTER(ctypes.c_double), ctypes.POINTER(ctypes.c_int64),
                                      ctypes.c_int]
@@ -291,6 +305,94 @@ class Handle:
             _ptr(_bf16(q_out)), _ld(q_out), _ptr(_bf16(k_pool)), _ptr(_bf16(v_pool)), k_pool.shape[0],
             _ptr(_bf16(out)), _ld(out), _ptr(ws), ws.numel(), _stream(stream)))
         return q_out, out
+
+    # ------------------------------------------------------------ contiguous-cache entries
+    def cache_workspace_bytes(self, n_tokens: int, n_groups: int, cache_rows: int, max_seq: int) -> int:
+        return int(_lib.dap_cache_workspace_bytes(self._h, n_tokens, n_groups, cache_rows, max_seq))
+
+    def _qkv(self, q, k, v):
+        ld = _ld(q)
+        if _ld(k) != ld or _ld(v) != ld:
+            raise ValueError("q, k and v must share one row stride")
+        return _ptr(_bf16(q)), _ptr(_bf16(k)), _ptr(_bf16(v)), ld
+
+    def _out(self, out, n, like):
+        m = self.model
+        return torch.empty(n, m.n_q_heads * m.head_dim, dtype=like.dtype, device=like.device) if out is None else out
+
+    def decode(self, q, k, v, pos: int, k_pool, v_pool, *, max_seq, q_gain=None, k_gain=None, out=None,
+               workspace=None, stream=None):
+        """One token per cache row, all at position pos. The cache: pools of
+        cache_rows * max_seq / 64 pages, row r owning pages r*max_seq/64 onward."""
+        R = q.shape[0]
+        out = self._out(out, R, q)
+        ws = self._workspace(workspace, self.cache_workspace_bytes(R, 1, R, max_seq), q)
+        _check(_lib.dap_decode(self._h, *self._qkv(q, k, v), R, pos, max_seq, _ptr(_bf16(q_gain)),
+                               _ptr(_bf16(k_gain)), _ptr(_bf16(k_pool)), _ptr(_bf16(v_pool)), _ptr(_bf16(out)),
+                               _ld(out), _ptr(ws), ws.numel(), _stream(stream)))
+        return out
+
+    def decode_rows(self, q, k, v, positions, k_pool, v_pool, *, max_seq, q_gain=None, k_gain=None, out=None,
+                    workspace=None, stream=None):
+        """One token per cache row, row b at positions[b]."""
+        R = q.shape[0]
+        out = self._out(out, R, q)
+        ws = self._workspace(workspace, self.cache_workspace_bytes(R, 1, R, max_seq), q)
+        _check(_lib.dap_decode_rows(self._h, *self._qkv(q, k, v), R, _ptr(_i32(positions)), max_seq,
+                                    _ptr(_bf16(q_gain)), _ptr(_bf16(k_gain)), _ptr(_bf16(k_pool)),
+                                    _ptr(_bf16(v_pool)), _ptr(_bf16(out)), _ld(out), _ptr(ws), ws.numel(),
+                                    _stream(stream)))
+        return out
+
+    def prefill(self, q, k, v, pos: int, k_pool, v_pool, *, cache_rows, max_seq, q_gain=None, k_gain=None,
+                out=None, workspace=None, stream=None):
+        """cache_rows * seq tokens: token b*seq+i is row b at position pos+i."""
+        T = q.shape[0]
+        seq = T // cache_rows
+        out = self._out(out, T, q)
+        ws = self._workspace(workspace, self.cache_workspace_bytes(T, cache_rows, cache_rows, max_seq), q)
+        _check(_lib.dap_prefill(self._h, *self._qkv(q, k, v), cache_rows, seq, pos, max_seq, _ptr(_bf16(q_gain)),
+                                _ptr(_bf16(k_gain)), _ptr(_bf16(k_pool)), _ptr(_bf16(v_pool)), _ptr(_bf16(out)),
+                                _ld(out), _ptr(ws), ws.numel(), _stream(stream)))
+        return out
+
+    def prefill_slots(self, q, k, v, slots, k_pool, v_pool, *, cache_rows, max_seq, q_gain=None, k_gain=None,
+                      out=None, workspace=None, stream=None):
+        """len(slots) prompts of seq tokens: token m*seq+i is row slots[m] at position i."""
+        T = q.shape[0]
+        M = slots.shape[0]
+        out = self._out(out, T, q)
+        ws = self._workspace(workspace, self.cache_workspace_bytes(T, M, cache_rows, max_seq), q)
+        _check(_lib.dap_prefill_slots(self._h, *self._qkv(q, k, v), M, T // M, _ptr(_i32(slots)), cache_rows,
+                                      max_seq, _ptr(_bf16(q_gain)), _ptr(_bf16(k_gain)), _ptr(_bf16(k_pool)),
+                                      _ptr(_bf16(v_pool)), _ptr(_bf16(out)), _ld(out), _ptr(ws), ws.numel(),
+                                      _stream(stream)))
+        return out
+
+    # ------------------------------------------------------------ in-pass entries (no cache)
+    def inpass_workspace_bytes(self, n_tokens: int, n_segments: int) -> int:
+        return int(_lib.dap_inpass_workspace_bytes(self._h, n_tokens, n_segments))
+
+    def packed(self, q, k, v, positions, segments, *, n_segments, q_gain=None, k_gain=None, out=None,
+               workspace=None, stream=None):
+        """Attention among the call's tokens: same segment, earlier or equal position."""
+        T = positions.shape[0]
+        out = self._out(out, T, q)
+        ws = self._workspace(workspace, self.inpass_workspace_bytes(T, n_segments), q)
+        _check(_lib.dap_packed(self._h, *self._qkv(q, k, v), T, _ptr(_i32(positions)), _ptr(_i32(segments)),
+                               n_segments, _ptr(_bf16(q_gain)), _ptr(_bf16(k_gain)), _ptr(_bf16(out)), _ld(out),
+                               _ptr(ws), ws.numel(), _stream(stream)))
+        return out
+
+    def forward(self, q, k, v, n_seqs: int, *, q_gain=None, k_gain=None, out=None, workspace=None, stream=None):
+        """n_seqs sequences of T/n_seqs tokens from position 0, no cache."""
+        T = q.shape[0]
+        out = self._out(out, T, q)
+        ws = self._workspace(workspace, self.inpass_workspace_bytes(T, n_seqs), q)
+        _check(_lib.dap_forward(self._h, *self._qkv(q, k, v), n_seqs, T // n_seqs, _ptr(_bf16(q_gain)),
+                                _ptr(_bf16(k_gain)), _ptr(_bf16(out)), _ld(out), _ptr(ws), ws.numel(),
+                                _stream(stream)))
+        return out
 
 
 def pools(n_pages: int, n_kv_heads: int, head_dim: int, device="cuda", dtype=torch.bfloat16):

@@ -3,6 +3,7 @@
 #include <cstdio>
 #include <cstring>
 #include <string>
+#include <algorithm>
 #include <unordered_set>
 #include <vector>
 
@@ -145,7 +146,7 @@ int end_validate(dap_handle* h, hipStream_t s) {
     if (err) {
         char buf[160];
         std::snprintf(buf, sizeof buf, "a kernel skipped out-of-range index entries (error bits 0x%x: 1 position, 2 row, "
-                      "4 page, 8 slot, 16 table width, 32 segment runs)", err);
+                      "4 page, 8 slot, 16 table width, 32 segment runs, 64 in-pass span)", err);
         return fail(DAP_BAD_INDEX, buf);
     }
     return DAP_OK;
@@ -347,6 +348,240 @@ int do_decode(dap_handle* h, const uint16_t* q, int64_t ld_q, int32_t n_rows, co
 
 size_t align256(size_t x) { return (x + 255) & ~size_t(255); }
 
+// ---------------------------------------------------------------- contiguous-cache and in-pass entries
+// Consecutive 256-byte aligned pieces of a workspace (sizes only when base is null).
+struct Carve {
+    char* base;
+    size_t off;
+    template <typename T>
+    T* take(size_t n) {
+        T* p = base ? reinterpret_cast<T*>(base + off) : nullptr;
+        off += align256(n * sizeof(T));
+        return p;
+    }
+};
+
+size_t attn_workspace(const dap_handle* h, long long n_tokens, int n_groups) {
+    size_t b = dap::prefill_workspace((int)n_tokens, n_groups, h->group);
+    if (n_tokens <= dap::kMaxDecodeRows) {
+        const dap::DecodePlan plan = dap::decode_plan((int)n_tokens, h->m.n_q_heads, h->m.n_kv_heads, h->m.head_dim,
+                                                      h->m.window, h->m.max_position);
+        b = std::max(b, plan.workspace_bytes);
+    }
+    return b;
+}
+
+struct CacheLayout {
+    int32_t* positions;
+    int32_t* rows;
+    int32_t* table;
+    uint16_t* q_rope;
+    char* attn;
+    size_t bytes;
+};
+
+CacheLayout cache_layout(const dap_handle* h, void* ws, long long n_tokens, int n_groups, int cache_rows, int max_seq) {
+    Carve c{static_cast<char*>(ws), 0};
+    CacheLayout L;
+    L.positions = c.take<int32_t>(n_tokens);
+    L.rows = c.take<int32_t>(n_tokens);
+    L.table = c.take<int32_t>((size_t)cache_rows * (max_seq / dap::kPage));
+    L.q_rope = c.take<uint16_t>((size_t)n_tokens * h->m.n_q_heads * h->m.head_dim);
+    L.attn = c.base ? c.base + c.off : nullptr;
+    L.bytes = c.off + attn_workspace(h, n_tokens, n_groups);
+    return L;
+}
+
+enum CacheKind { kCacheDecode, kCacheDecodeRows, kCachePrefill, kCachePrefillSlots };
+
+// The contiguous-cache entries: identity table and per-token positions/rows
+// built on the device, then the write and the paged prefill or decode.
+int do_cache(dap_handle* h, CacheKind kind, const uint16_t* q, const uint16_t* k, const uint16_t* v, int64_t ld_in,
+             int32_t n_groups, int32_t per_group, int32_t pos, const int32_t* positions, const int32_t* slot_rows,
+             int32_t cache_rows, int32_t max_seq, const uint16_t* q_gain, const uint16_t* k_gain, uint16_t* k_pool,
+             uint16_t* v_pool, uint16_t* out, int64_t ld_out, void* ws, size_t ws_bytes, hipStream_t s) {
+    if (int rc = check_handle(h)) return rc;
+    DAP_REQUIRE(n_groups >= 0 && per_group >= 0 && cache_rows >= 0, DAP_INVALID_ARG, "counts must be >= 0");
+    DAP_REQUIRE(max_seq > 0 && max_seq % dap::kPage == 0, DAP_INVALID_ARG, "max_seq must be a positive multiple of 64");
+    const long long n = (long long)n_groups * per_group;
+    if (n == 0) return DAP_OK;
+    DAP_REQUIRE(n < (1ll << 30), DAP_UNSUPPORTED, "too many tokens for one call");
+    const int ppr = max_seq / dap::kPage;
+    DAP_REQUIRE(cache_rows > 0 && (long long)cache_rows * ppr * dap::kPage < (1ll << 31), DAP_INVALID_ARG,
+                "the cache must have rows and fewer than 2^31 slots");
+    const int limit = std::min(max_seq, h->m.max_position);
+    if (kind == kCacheDecode || kind == kCachePrefill)
+        DAP_REQUIRE(pos >= 0 && (long long)pos + per_group <= limit, DAP_INVALID_ARG,
+                    "positions must lie in [0, min(max_seq, max_position))");
+    if (kind == kCacheDecodeRows)
+        DAP_REQUIRE(positions && aligned4(positions), DAP_INVALID_ARG, "positions must be a non-null aligned pointer");
+    if (kind == kCachePrefillSlots) {
+        DAP_REQUIRE(slot_rows && aligned4(slot_rows), DAP_INVALID_ARG, "slots must be a non-null aligned pointer");
+        DAP_REQUIRE(per_group <= limit, DAP_INVALID_ARG, "seq must be <= min(max_seq, max_position)");
+    }
+    const CacheLayout L = cache_layout(h, ws, n, n_groups, cache_rows, max_seq);
+    DAP_REQUIRE(ws && ws_bytes >= L.bytes && aligned16(ws), DAP_WORKSPACE_TOO_SMALL,
+                "workspace must be 16-byte aligned and at least dap_cache_workspace_bytes()");
+    if (h->validate && kind == kCachePrefillSlots) {
+        std::vector<int32_t> hs;
+        if (!to_host(hs, slot_rows, n_groups, s)) return fail(DAP_HIP_ERROR, "copying slots");
+        std::unordered_set<int32_t> seen;
+        for (int32_t r : hs) {
+            if (r < 0 || r >= cache_rows) return fail(DAP_BAD_INDEX, "cache row " + std::to_string(r) + " out of range");
+            if (!seen.insert(r).second) return fail(DAP_BAD_INDEX, "two prompts fill cache row " + std::to_string(r));
+        }
+    }
+    dap::LayoutPrep lp;
+    lp.mode = kind == kCacheDecode ? dap::kLayoutConstPos
+              : kind == kCachePrefill ? dap::kLayoutSpan
+              : kind == kCachePrefillSlots ? dap::kLayoutSlots : dap::kLayoutRowsOnly;
+    lp.n_tokens = (int)n;
+    lp.per_group = per_group;
+    lp.base_pos = pos;
+    lp.row_map = slot_rows;
+    lp.positions = kind == kCacheDecodeRows ? nullptr : L.positions;
+    lp.rows = L.rows;
+    lp.table = L.table;
+    lp.table_rows = cache_rows;
+    lp.table_ld = ppr;
+    hipError_t e = dap::launch_layout_prep(lp, s, h->profiler());
+    if (e != hipSuccess) return hip_fail(e, "index preparation launch");
+    const int32_t* P = kind == kCacheDecodeRows ? positions : L.positions;
+    const int n_pages = cache_rows * ppr;
+    const int64_t wq = (int64_t)h->m.n_q_heads * h->m.head_dim;
+    int rc = do_write(h, q, k, v, ld_in, (int)n, P, L.rows, nullptr, L.table, ppr, cache_rows, q_gain, k_gain, L.q_rope,
+                      wq, k_pool, v_pool, n_pages, s);
+    if (rc) return rc;
+    const size_t attn_bytes = ws_bytes - (size_t)(L.attn - static_cast<char*>(ws));
+    if (kind == kCacheDecode || kind == kCacheDecodeRows)
+        return do_decode(h, L.q_rope, wq, (int)n, P, L.rows, L.table, ppr, cache_rows, k_pool, v_pool, n_pages, out,
+                         ld_out, L.attn, attn_bytes, s);
+    return do_prefill(h, L.q_rope, wq, (int)n, P, L.rows, n_groups, L.table, ppr, cache_rows, k_pool, v_pool, n_pages,
+                      out, ld_out, L.attn, attn_bytes, s);
+}
+
+struct InpassLayout {
+    int32_t* positions;   // dap_forward's generated positions
+    int32_t* segments;    // and segments
+    int32_t* table;
+    int32_t* slots;
+    int32_t* rel;
+    uint16_t* q_rope;
+    char* prefill;
+    uint16_t* k_pool;
+    uint16_t* v_pool;
+    int table_ld;
+    int capacity;
+    size_t bytes;
+};
+
+InpassLayout inpass_layout(const dap_handle* h, void* ws, long long n_tokens, int n_segments) {
+    Carve c{static_cast<char*>(ws), 0};
+    InpassLayout L;
+    L.table_ld = (int)((n_tokens + dap::kPage - 1) / dap::kPage);
+    L.capacity = L.table_ld + n_segments;
+    L.positions = c.take<int32_t>(n_tokens);
+    L.segments = c.take<int32_t>(n_tokens);
+    L.table = c.take<int32_t>((size_t)n_segments * L.table_ld);
+    L.slots = c.take<int32_t>(n_tokens);
+    L.rel = c.take<int32_t>(n_tokens);
+    L.q_rope = c.take<uint16_t>((size_t)n_tokens * h->m.n_q_heads * h->m.head_dim);
+    L.prefill = c.base ? c.base + c.off : nullptr;
+    c.off += align256(dap::prefill_workspace((int)n_tokens, n_segments, h->group));
+    const size_t tile = (size_t)h->m.n_kv_heads * dap::kPage * h->m.head_dim;
+    L.k_pool = c.take<uint16_t>((size_t)L.capacity * tile);
+    L.v_pool = c.take<uint16_t>((size_t)L.capacity * tile);
+    L.bytes = c.off;
+    return L;
+}
+
+// Host check for the in-pass entries: each segment one run of the pack,
+// holding consecutive distinct positions.
+int check_inpass(const std::vector<int32_t>& pos, const std::vector<int32_t>& seg, int n_segments) {
+    std::vector<std::vector<int32_t>> by(n_segments);
+    std::vector<int> last_run(n_segments, -1);
+    for (size_t t = 0; t < pos.size(); ++t) {
+        const int sg = seg[t];
+        if (sg < 0 || sg >= n_segments) return fail(DAP_BAD_INDEX, "segment id out of range at " + std::to_string(t));
+        if (last_run[sg] >= 0 && last_run[sg] != (int)t - 1)
+            return fail(DAP_BAD_INDEX, "segment " + std::to_string(sg) + " is not one run of the pack");
+        last_run[sg] = (int)t;
+        by[sg].push_back(pos[t]);
+    }
+    for (int sg = 0; sg < n_segments; ++sg) {
+        std::vector<int32_t>& v = by[sg];
+        std::sort(v.begin(), v.end());
+        for (size_t i = 1; i < v.size(); ++i)
+            if (v[i] != v[i - 1] + 1)
+                return fail(DAP_BAD_INDEX, "segment " + std::to_string(sg) + " positions are not consecutive and distinct");
+    }
+    return DAP_OK;
+}
+
+int do_inpass(dap_handle* h, const uint16_t* q, const uint16_t* k, const uint16_t* v, int64_t ld_in,
+              long long n, const int32_t* positions, const int32_t* segments, int32_t n_segments, int32_t seq,
+              const uint16_t* q_gain, const uint16_t* k_gain, uint16_t* out, int64_t ld_out, void* ws,
+              size_t ws_bytes, hipStream_t s) {
+    if (int rc = check_handle(h)) return rc;
+    DAP_REQUIRE(n >= 0, DAP_INVALID_ARG, "counts must be >= 0");
+    if (n == 0) return DAP_OK;
+    DAP_REQUIRE(n < (1ll << 30), DAP_UNSUPPORTED, "too many tokens for one call");
+    DAP_REQUIRE(n_segments > 0 && n_segments <= dap::kMaxInpassSegments, DAP_UNSUPPORTED,
+                "in-pass entries take 1 to 4096 segments");
+    const InpassLayout L = inpass_layout(h, ws, n, n_segments);
+    DAP_REQUIRE((long long)L.capacity * dap::kPage < (1ll << 31), DAP_UNSUPPORTED, "too many tokens for one call");
+    DAP_REQUIRE(ws && ws_bytes >= L.bytes && aligned16(ws), DAP_WORKSPACE_TOO_SMALL,
+                "workspace must be 16-byte aligned and at least dap_inpass_workspace_bytes()");
+    const bool generated = positions == nullptr;     // dap_forward
+    if (generated) {
+        DAP_REQUIRE(seq <= h->m.max_position, DAP_INVALID_ARG, "seq must be <= the model's max_position");
+        dap::LayoutPrep lp;
+        lp.mode = dap::kLayoutSpan;
+        lp.n_tokens = (int)n;
+        lp.per_group = seq;
+        lp.base_pos = 0;
+        lp.row_map = nullptr;
+        lp.positions = L.positions;
+        lp.rows = L.segments;
+        lp.table = nullptr;
+        lp.table_rows = 0;
+        lp.table_ld = 0;
+        hipError_t e = dap::launch_layout_prep(lp, s, h->profiler());
+        if (e != hipSuccess) return hip_fail(e, "index preparation launch");
+        positions = L.positions;
+        segments = L.segments;
+    } else {
+        DAP_REQUIRE(aligned4(positions) && segments && aligned4(segments), DAP_INVALID_ARG,
+                    "positions and segments must be non-null aligned pointers");
+        if (h->validate) {
+            std::vector<int32_t> hp, hs;
+            if (!to_host(hp, positions, n, s) || !to_host(hs, segments, n, s))
+                return fail(DAP_HIP_ERROR, "copying index arrays");
+            if (int rc = check_inpass(hp, hs, n_segments)) return rc;
+        }
+    }
+    dap::InpassPrep ip;
+    ip.positions = positions;
+    ip.segments = segments;
+    ip.n_tokens = (int)n;
+    ip.n_segments = n_segments;
+    ip.table = L.table;
+    ip.table_ld = L.table_ld;
+    ip.capacity = L.capacity;
+    ip.slots = L.slots;
+    ip.rel_positions = L.rel;
+    ip.err = h->d_err;
+    hipError_t e = dap::launch_inpass_prep(ip, s, h->profiler());
+    if (e != hipSuccess) return hip_fail(e, "in-pass preparation launch");
+    const int64_t wq = (int64_t)h->m.n_q_heads * h->m.head_dim;
+    int rc = do_write(h, q, k, v, ld_in, (int)n, positions, nullptr, L.slots, nullptr, 0, 0, q_gain, k_gain, L.q_rope,
+                      wq, L.k_pool, L.v_pool, L.capacity, s);
+    if (rc) return rc;
+    return do_prefill(h, L.q_rope, wq, (int)n, L.rel, segments, n_segments, L.table, L.table_ld, n_segments,
+                      L.k_pool, L.v_pool, L.capacity, out, ld_out, L.prefill,
+                      ws_bytes - (size_t)(L.prefill - static_cast<char*>(ws)), s);
+}
+
 }  // namespace
 
 extern "C" {
@@ -536,6 +771,70 @@ int dap_step_paged(dap_handle* h, const uint16_t* q, const uint16_t* k, const ui
         if (rc) return rc;
     }
     return DAP_OK;
+}
+
+size_t dap_cache_workspace_bytes(const dap_handle* h, int32_t n_tokens, int32_t n_groups, int32_t cache_rows,
+                                 int32_t max_seq) {
+    if (!h || n_tokens < 0 || n_groups < 0 || cache_rows < 0 || max_seq <= 0 || max_seq % dap::kPage) return 0;
+    return cache_layout(h, nullptr, n_tokens, std::max(n_groups, 1), cache_rows, max_seq).bytes;
+}
+
+int dap_decode(dap_handle* h, const uint16_t* q, const uint16_t* k, const uint16_t* v, int64_t ld_in,
+               int32_t cache_rows, int32_t pos, int32_t max_seq, const uint16_t* q_gain, const uint16_t* k_gain,
+               uint16_t* k_pool, uint16_t* v_pool, uint16_t* out, int64_t ld_out, void* workspace,
+               size_t workspace_bytes, void* stream) {
+    return do_cache(h, kCacheDecode, q, k, v, ld_in, cache_rows, 1, pos, nullptr, nullptr, cache_rows, max_seq, q_gain,
+                    k_gain, k_pool, v_pool, out, ld_out, workspace, workspace_bytes, static_cast<hipStream_t>(stream));
+}
+
+int dap_decode_rows(dap_handle* h, const uint16_t* q, const uint16_t* k, const uint16_t* v, int64_t ld_in,
+                    int32_t cache_rows, const int32_t* positions, int32_t max_seq, const uint16_t* q_gain,
+                    const uint16_t* k_gain, uint16_t* k_pool, uint16_t* v_pool, uint16_t* out, int64_t ld_out,
+                    void* workspace, size_t workspace_bytes, void* stream) {
+    return do_cache(h, kCacheDecodeRows, q, k, v, ld_in, cache_rows, 1, 0, positions, nullptr, cache_rows, max_seq,
+                    q_gain, k_gain, k_pool, v_pool, out, ld_out, workspace, workspace_bytes,
+                    static_cast<hipStream_t>(stream));
+}
+
+int dap_prefill(dap_handle* h, const uint16_t* q, const uint16_t* k, const uint16_t* v, int64_t ld_in,
+                int32_t cache_rows, int32_t seq, int32_t pos, int32_t max_seq, const uint16_t* q_gain,
+                const uint16_t* k_gain, uint16_t* k_pool, uint16_t* v_pool, uint16_t* out, int64_t ld_out,
+                void* workspace, size_t workspace_bytes, void* stream) {
+    return do_cache(h, kCachePrefill, q, k, v, ld_in, cache_rows, seq, pos, nullptr, nullptr, cache_rows, max_seq,
+                    q_gain, k_gain, k_pool, v_pool, out, ld_out, workspace, workspace_bytes,
+                    static_cast<hipStream_t>(stream));
+}
+
+int dap_prefill_slots(dap_handle* h, const uint16_t* q, const uint16_t* k, const uint16_t* v, int64_t ld_in,
+                      int32_t n_prompts, int32_t seq, const int32_t* slots, int32_t cache_rows, int32_t max_seq,
+                      const uint16_t* q_gain, const uint16_t* k_gain, uint16_t* k_pool, uint16_t* v_pool,
+                      uint16_t* out, int64_t ld_out, void* workspace, size_t workspace_bytes, void* stream) {
+    return do_cache(h, kCachePrefillSlots, q, k, v, ld_in, n_prompts, seq, 0, nullptr, slots, cache_rows, max_seq,
+                    q_gain, k_gain, k_pool, v_pool, out, ld_out, workspace, workspace_bytes,
+                    static_cast<hipStream_t>(stream));
+}
+
+size_t dap_inpass_workspace_bytes(const dap_handle* h, int32_t n_tokens, int32_t n_segments) {
+    if (!h || n_tokens < 0 || n_segments <= 0) return 0;
+    return inpass_layout(h, nullptr, n_tokens, n_segments).bytes;
+}
+
+int dap_packed(dap_handle* h, const uint16_t* q, const uint16_t* k, const uint16_t* v, int64_t ld_in,
+               int32_t n_tokens, const int32_t* positions, const int32_t* segments, int32_t n_segments,
+               const uint16_t* q_gain, const uint16_t* k_gain, uint16_t* out, int64_t ld_out, void* workspace,
+               size_t workspace_bytes, void* stream) {
+    if (n_tokens > 0 && !positions) return fail(DAP_INVALID_ARG, "positions must be a non-null aligned pointer");
+    return do_inpass(h, q, k, v, ld_in, n_tokens, positions, segments, n_segments, 0, q_gain, k_gain, out, ld_out,
+                     workspace, workspace_bytes, static_cast<hipStream_t>(stream));
+}
+
+int dap_forward(dap_handle* h, const uint16_t* q, const uint16_t* k, const uint16_t* v, int64_t ld_in,
+                int32_t n_seqs, int32_t seq, const uint16_t* q_gain, const uint16_t* k_gain, uint16_t* out,
+                int64_t ld_out, void* workspace, size_t workspace_bytes, void* stream) {
+    if (int rc = check_handle(h)) return rc;
+    DAP_REQUIRE(n_seqs >= 0 && seq >= 0, DAP_INVALID_ARG, "counts must be >= 0");
+    return do_inpass(h, q, k, v, ld_in, (long long)n_seqs * seq, nullptr, nullptr, n_seqs, seq, q_gain, k_gain, out,
+                     ld_out, workspace, workspace_bytes, static_cast<hipStream_t>(stream));
 }
 
 }  // extern "C"

@@ -20,6 +20,8 @@ enum ErrorBits : unsigned {
     kErrPage = 4u,
     kErrSlot = 8u,
     kErrTable = 16u,
+    // 32 is the prefill's segment-run overflow (prefill.hip)
+    kErrSpan = 64u,      // an in-pass segment's positions do not fit its scratch pages
 };
 
 typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
@@ -145,5 +147,44 @@ hipError_t launch_decode(const AttnArgs& a, const DecodePlan& plan, void* worksp
 // Prefill: tile list sizing and launch.
 size_t prefill_workspace(int n_tokens, int n_segments, int group);
 hipError_t launch_prefill(const AttnArgs& a, int n_segments, void* workspace, hipStream_t s, Profiler* prof);
+
+// Index preparation for the contiguous-cache entries: per-token positions and
+// rows for tokens laid out [groups][per_group], and an identity page table.
+enum LayoutMode : int {
+    kLayoutConstPos = 0,   // position = base_pos, row = token
+    kLayoutSpan = 1,       // position = base_pos + i, row = group
+    kLayoutSlots = 2,      // position = i, row = row_map[group]
+    kLayoutRowsOnly = 3,   // row = token (positions given by the caller)
+};
+struct LayoutPrep {
+    int mode;
+    int n_tokens;
+    int per_group;
+    int base_pos;
+    const int32_t* row_map;
+    int32_t* positions;     // may be null (kLayoutRowsOnly)
+    int32_t* rows;
+    int32_t* table;         // identity table [table_rows][table_ld], may be null
+    int table_rows;
+    int table_ld;
+};
+hipError_t launch_layout_prep(const LayoutPrep& p, hipStream_t s, Profiler* prof);
+
+// Index preparation for the in-pass entries (no cache): each segment's keys
+// go to scratch pages, packed segment after segment from its first position.
+constexpr int kMaxInpassSegments = 4096;
+struct InpassPrep {
+    const int32_t* positions;
+    const int32_t* segments;
+    int n_tokens;
+    int n_segments;
+    int32_t* table;         // [n_segments][table_ld] scratch page ids, -1 past a segment
+    int table_ld;
+    int capacity;           // scratch pages
+    int32_t* slots;         // [n_tokens] scratch slot of each token, -1 if it does not fit
+    int32_t* rel_positions; // [n_tokens] position minus its segment's first position
+    unsigned* err;
+};
+hipError_t launch_inpass_prep(const InpassPrep& p, hipStream_t s, Profiler* prof);
 
 }  // namespace dap

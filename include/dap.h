@@ -210,6 +210,102 @@ int dap_step_paged(dap_handle* handle,
     void* workspace, size_t workspace_bytes, void* stream);
 
 /*
+ * Contiguous-cache entries.
+ * ("Phi-3 Mini 4K Instruct" files, src/attention.linnet: decode, prefill,
+ * decode_rows and prefill_slots, the entries that keep [Batch, Heads,
+ * MaxSeq, D] caches; model card, Entries.)
+ *
+ * A cache of cache_rows rows and max_seq positions (max_seq a positive
+ * multiple of 64) is held as a page pool of cache_rows * max_seq / 64 pages
+ * in the layout above, row r owning pages r*max_seq/64 .. (r+1)*max_seq/64-1;
+ * k_pool and v_pool are those pools (the caller allocates and keeps them).
+ * Each call writes its tokens' roped k and raw v into the cache (as
+ * dap_rope_qknorm_write_pages) and returns the attention output of every
+ * token (as the paged prefill/decode over that table).
+ * q, k, v : the fused projection rows of the call's tokens, [n][ld_in] bf16.
+ * q_gain, k_gain : as for the write (required iff the model has QK-norm).
+ * out : [n][ld_out] bf16.
+ *  dap_decode       : n = cache_rows tokens; token b is row b at position pos.
+ *  dap_decode_rows  : n = cache_rows tokens; token b is row b at positions[b]
+ *                     (device int32).
+ *  dap_prefill      : n = cache_rows * seq tokens; token b*seq+i is row b at
+ *                     position pos + i (each row's queries see that row up to
+ *                     their own position, earlier calls' keys included).
+ *  dap_prefill_slots: n = n_prompts * seq tokens; token m*seq+i is row
+ *                     slots[m] (device int32, distinct, < cache_rows) at
+ *                     position i, so each prompt sees only itself. Prompts
+ *                     shorter than seq are padded by the caller; padding tokens
+ *                     are written and attended like the rest, and real tokens
+ *                     never see them (they come later).
+ * workspace : at least dap_cache_workspace_bytes(handle, n, groups,
+ *             cache_rows, max_seq) with groups = 1 for the decodes, cache_rows
+ *             for dap_prefill and n_prompts for dap_prefill_slots.
+ * Positions must be < min(max_seq, the model's max_position): the scalar pos
+ * is checked on the host; device arrays in validate mode, and otherwise by
+ * the kernels' bounds checks (out-of-range entries are skipped and flagged).
+ */
+size_t dap_cache_workspace_bytes(const dap_handle* handle, int32_t n_tokens, int32_t n_groups,
+                                 int32_t cache_rows, int32_t max_seq);
+int dap_decode(dap_handle* handle,
+    const uint16_t* q, const uint16_t* k, const uint16_t* v, int64_t ld_in,
+    int32_t cache_rows, int32_t pos, int32_t max_seq,
+    const uint16_t* q_gain, const uint16_t* k_gain,
+    uint16_t* k_pool, uint16_t* v_pool, uint16_t* out, int64_t ld_out,
+    void* workspace, size_t workspace_bytes, void* stream);
+int dap_decode_rows(dap_handle* handle,
+    const uint16_t* q, const uint16_t* k, const uint16_t* v, int64_t ld_in,
+    int32_t cache_rows, const int32_t* positions, int32_t max_seq,
+    const uint16_t* q_gain, const uint16_t* k_gain,
+    uint16_t* k_pool, uint16_t* v_pool, uint16_t* out, int64_t ld_out,
+    void* workspace, size_t workspace_bytes, void* stream);
+int dap_prefill(dap_handle* handle,
+    const uint16_t* q, const uint16_t* k, const uint16_t* v, int64_t ld_in,
+    int32_t cache_rows, int32_t seq, int32_t pos, int32_t max_seq,
+    const uint16_t* q_gain, const uint16_t* k_gain,
+    uint16_t* k_pool, uint16_t* v_pool, uint16_t* out, int64_t ld_out,
+    void* workspace, size_t workspace_bytes, void* stream);
+int dap_prefill_slots(dap_handle* handle,
+    const uint16_t* q, const uint16_t* k, const uint16_t* v, int64_t ld_in,
+    int32_t n_prompts, int32_t seq, const int32_t* slots, int32_t cache_rows, int32_t max_seq,
+    const uint16_t* q_gain, const uint16_t* k_gain,
+    uint16_t* k_pool, uint16_t* v_pool, uint16_t* out, int64_t ld_out,
+    void* workspace, size_t workspace_bytes, void* stream);
+
+/*
+ * In-pass entries: attention among the call's own tokens, no cache.
+ * ("Phi-3 Mini 4K Instruct" files, src/attention.linnet: packed, the
+ * training form of prefill_packed with no cache written, and forward, whole
+ * sequences from position 0.)
+ *
+ * dap_packed : token t is position positions[t] of segment segments[t]
+ *   (0 <= segments[t] < n_segments <= 4096); it attends to the tokens of its
+ *   own segment whose positions are <= its own and within the window. Each
+ *   segment's tokens must be one contiguous run of the pack (prompts packed
+ *   end to end) and hold consecutive, distinct positions (validate mode
+ *   checks both).
+ * dap_forward : n_seqs sequences of seq tokens, token b*seq+i at position i
+ *   of sequence b.
+ * q, k, v : fused projection rows [n][ld_in]; out : [n][ld_out] bf16.
+ * The tokens' roped k and v go to scratch pages inside the workspace (at
+ * least dap_inpass_workspace_bytes(handle, n, n_segments), n_segments =
+ * n_seqs for dap_forward), then the paged prefill runs over them with
+ * positions counted from each segment's first position.
+ */
+size_t dap_inpass_workspace_bytes(const dap_handle* handle, int32_t n_tokens, int32_t n_segments);
+int dap_packed(dap_handle* handle,
+    const uint16_t* q, const uint16_t* k, const uint16_t* v, int64_t ld_in,
+    int32_t n_tokens, const int32_t* positions, const int32_t* segments, int32_t n_segments,
+    const uint16_t* q_gain, const uint16_t* k_gain,
+    uint16_t* out, int64_t ld_out,
+    void* workspace, size_t workspace_bytes, void* stream);
+int dap_forward(dap_handle* handle,
+    const uint16_t* q, const uint16_t* k, const uint16_t* v, int64_t ld_in,
+    int32_t n_seqs, int32_t seq,
+    const uint16_t* q_gain, const uint16_t* k_gain,
+    uint16_t* out, int64_t ld_out,
+    void* workspace, size_t workspace_bytes, void* stream);
+
+/*
  * Kernel timing, for measurement (default off; not one of the pages'
  * operations). While on, every kernel the library launches is bracketed by
  * a pair of hipEvents recorded on its launch stream; dap_profile_read
@@ -225,7 +321,8 @@ enum {
     DAP_KERNEL_PREFILL = 2,        /* the prefill's attention kernel */
     DAP_KERNEL_DECODE = 3,         /* the decode kernel */
     DAP_KERNEL_DECODE_MERGE = 4,   /* the decode's cross-chunk merge */
-    DAP_N_KERNELS = 5
+    DAP_KERNEL_PREP = 5,           /* index preparation of the contiguous and in-pass entries */
+    DAP_N_KERNELS = 6
 };
 int dap_set_profiling(dap_handle* handle, int on);
 int dap_profile_read(dap_handle* handle, double* total_ms, int64_t* launches, int reset);
