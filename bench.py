@@ -158,6 +158,32 @@ class Bench:
             self.tokens = T + 4
             self.desc = ("phi-3-mini-shaped: prefill_packed of 4096 tokens (prompts 512/1024/1536/1024, window "
                          "2047, Hq=Hkv=32, D96) then decode_paged of the 4 rows at position 3000")
+        elif name == "mistral_contiguous":
+            R = wl.n_dec
+            self.qkv = wl.qkv("step", R, "cuda")
+            self.pos = i32(wl.dec_positions)
+            self.out = torch.empty(R, hq * D, dtype=torch.int16, device="cuda")
+            self.max_seq = wl.table.shape[1] * 64
+            self.ws = self.h.workspace(self.h.cache_workspace_bytes(R, 1, R, self.max_seq))
+            self.dec_bytes = decode_bytes(m, wl.dec_positions)
+            self.bytes = write_bytes(m, R) + self.dec_bytes
+            self.flops = 0.0
+            self.tokens = R
+            self.desc = ("mistral-7b-shaped decode_rows on a contiguous cache: 64 rows of MaxSeq 32768 (identity "
+                         "table), contexts U[1024,32768], Hq32/Hkv8/D128")
+        elif name == "packed_train":
+            T = wl.n_pre
+            self.qkv = wl.qkv("train", T, "cuda")
+            self.pos, self.seg = i32(wl.pre_positions), i32(wl.pre_segments)
+            self.out = torch.empty(T, hq * D, dtype=torch.int16, device="cuda")
+            self.n_seg = int(wl.pre_segments.max()) + 1
+            self.ws = self.h.workspace(self.h.inpass_workspace_bytes(T, self.n_seg))
+            self.flops = prefill_flops(m, wl.pre_positions)
+            self.bytes = write_bytes(m, T) + prefill_bytes(m, wl.pre_positions, wl.pre_segments)
+            self.dec_bytes = 0
+            self.tokens = T
+            self.desc = ("llama-3.1-8b-shaped packed training forward (no cache): 8 prompts of 4096 tokens packed "
+                         "end to end, positions 0..4095 each, Hq32/Hkv8/D128, theta 5e5 + llama3")
         else:
             raise SystemExit(f"unknown workload {name}")
         D = m.head_dim
@@ -179,6 +205,11 @@ class Bench:
                                       q_out=self.q_out)
             h.attn_prefill_packed(self.q_out, self.pos, self.seg, self.table, self.kp, self.vp, n_segments=1,
                                   out=self.out, workspace=self.ws)
+        elif self.name == "mistral_contiguous":
+            h.decode_rows(*self.split, self.pos, self.kp, self.vp, max_seq=self.max_seq, out=self.out,
+                          workspace=self.ws)
+        elif self.name == "packed_train":
+            h.packed(*self.split, self.pos, self.seg, n_segments=self.n_seg, out=self.out, workspace=self.ws)
         elif self.name == "phi3":
             h.rope_qknorm_write_pages(*self.split, self.pos, self.kp, self.vp, rows=self.seg, table=self.table,
                                       q_out=self.q_out)
@@ -207,7 +238,9 @@ def cpu_baseline(b: Bench, budget_s: float = 20.0):
         tok_pos, tok_rows = b.pos_np, b.rows_np
         pre_pick = np.arange(wl.n_pre)
         dec_pick = np.arange(wl.n_dec)
-    elif b.name == "mistral":
+    elif b.name == "packed_train":
+        return cpu_baseline_inpass(b, freqs, threads)
+    elif b.name in ("mistral", "mistral_contiguous"):
         tok_pos, tok_rows = wl.dec_positions, wl.dec_rows
         pre_pick = np.zeros(0, int)
         dec_pick = np.arange(wl.n_dec)
@@ -268,6 +301,33 @@ def cpu_baseline(b: Bench, budget_s: float = 20.0):
             "sample": sample, "seconds": round(dt, 2)}
 
 
+def cpu_baseline_inpass(b: Bench, freqs, threads):
+    """The oracle on the packed training forward: the front half of every
+    token, then the in-pass attention of a spread of query tokens of the
+    first prompt (each over its prompt's keys up to itself)."""
+    from oracle import attention, bf16, core
+
+    wl, m = b.wl, b.m
+    qkv_np = b.qkv.cpu().numpy().view(np.uint16)
+    pos, seg = wl.pre_positions, wl.pre_segments
+    t0 = time.perf_counter()
+    q, k, vb = core.prepare_tokens(qkv_np, pos, m.n_q_heads, m.n_kv_heads, m.head_dim, freqs)
+    qf, kf, vf = bf16.round_f64(q), bf16.round_f64(k), bf16.to_f64(vb)
+    first = np.nonzero(seg == 0)[0]
+    order = first[np.argsort(pos[first])]
+    K, V = np.swapaxes(kf[order], 0, 1), np.swapaxes(vf[order], 0, 1)
+    picks = order[np.linspace(0, len(order) - 1, 240).astype(int)]
+    flops = 0.0
+    for t in picks:
+        attention.attend_one(qf[t], K, V, int(pos[t]), m.window)
+        flops += 4.0 * m.head_dim * m.n_q_heads * (int(pos[t]) + 1)
+    dt = time.perf_counter() - t0
+    sample = (f"oracle front half of all {len(pos)} tokens, then in-pass attention of {len(picks)} query tokens of the first "
+              f"prompt; {flops / 1e9:.2f} GFLOP of attention in {dt:.1f} s (front half included in the time)")
+    return {"value": round(flops / dt / 1e12, 6), "unit": "TFLOP/s", "cores": int(threads), "kind": "oracle",
+            "sample": sample, "seconds": round(dt, 2)}
+
+
 # --------------------------------------------------------------------------- copy ceiling
 def copy_ceiling(nbytes: int = 1 << 30, reps: int = 10) -> float:
     """Measured device-to-device copy rate (bytes read + bytes written per
@@ -311,7 +371,8 @@ def main():
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=20)
     ap.add_argument("--warmup", type=int, default=3)
-    ap.add_argument("--workload", default="qwen3", choices=["qwen3", "mistral", "llama31", "phi3"])
+    ap.add_argument("--workload", default="qwen3",
+                    choices=["qwen3", "mistral", "llama31", "phi3", "mistral_contiguous", "packed_train"])
     ap.add_argument("--no-cpu-baseline", action="store_true")
     args = ap.parse_args()
     if args.gpus != 1:

@@ -317,4 +317,29 @@ def qwen3() -> Workload:
                     dec_positions=dec_p, dec_rows=np.arange(8, 136, dtype=np.int32))
 
 
-ALL = {"tiny": tiny, "phi3": phi3, "mistral": mistral, "llama31": llama31, "qwen3": qwen3}
+def mistral_contiguous() -> Workload:
+    """The Mistral decode rows on a contiguous cache: 64 rows of MaxSeq 32768,
+    row r owning pages 512r .. 512r + 511 (the identity table), same
+    contexts as mistral()."""
+    src = mistral()
+    table = np.arange(64 * 512, dtype=np.int32).reshape(64, 512)
+    return Workload("mistral_contiguous", src.model, 64 * 512, table, dec_positions=src.dec_positions,
+                    dec_rows=src.dec_rows)
+
+
+PACKED_PROMPTS = 8
+PACKED_LEN = 4096
+
+
+def packed_train() -> Workload:
+    """A packed training forward on the Llama-3.1-8B shape: 8 prompts of 4096
+    tokens packed end to end, each at positions 0..4095, attending among
+    themselves (no cache, so no pool)."""
+    m = ModelShape("llama31", 32, 8, 128, 5e5, llama3=(8.0, 1.0, 4.0, 8192.0), max_position=65536)
+    pos = np.tile(np.arange(PACKED_LEN, dtype=np.int32), PACKED_PROMPTS)
+    seg = np.repeat(np.arange(PACKED_PROMPTS, dtype=np.int32), PACKED_LEN)
+    return Workload("packed_train", m, 0, np.zeros((0, 1), np.int32), pre_positions=pos, pre_segments=seg)
+
+
+ALL = {"tiny": tiny, "phi3": phi3, "mistral": mistral, "llama31": llama31, "qwen3": qwen3,
+       "mistral_contiguous": mistral_contiguous, "packed_train": packed_train}
