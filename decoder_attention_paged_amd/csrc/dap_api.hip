@@ -76,6 +76,9 @@ struct dap_handle {
     int validate;
     dap::ProfilerState* prof_state;
     dap::Profiler prof;
+    // step_paged runs its prefill on this second stream, beside the decode
+    hipStream_t side;
+    hipEvent_t fork_ev, join_ev;
     dap::Profiler* profiler() { return prof_state ? &prof : nullptr; }
 };
 
@@ -618,6 +621,9 @@ int dap_create(const dap_model* mp, dap_handle** out) {
     h->d_err = nullptr;
     h->prof_state = nullptr;
     h->prof.st = nullptr;
+    h->side = nullptr;
+    h->fork_ev = nullptr;
+    h->join_ev = nullptr;
     h->h_inv_freq = build_inv_freq(m);
     hipError_t e = hipGetDevice(&h->device);
     if (e == hipSuccess) e = hipMalloc(&h->d_inv_freq, h->h_inv_freq.size() * sizeof(double));
@@ -625,6 +631,9 @@ int dap_create(const dap_model* mp, dap_handle** out) {
     if (e == hipSuccess)
         e = hipMemcpy(h->d_inv_freq, h->h_inv_freq.data(), h->h_inv_freq.size() * sizeof(double), hipMemcpyHostToDevice);
     if (e == hipSuccess) e = hipMemset(h->d_err, 0, 256);
+    if (e == hipSuccess) e = hipStreamCreateWithFlags(&h->side, hipStreamNonBlocking);   // default priority
+    if (e == hipSuccess) e = hipEventCreateWithFlags(&h->fork_ev, hipEventDisableTiming);
+    if (e == hipSuccess) e = hipEventCreateWithFlags(&h->join_ev, hipEventDisableTiming);
     if (e != hipSuccess) {
         dap_destroy(h);
         return hip_fail(e, "dap_create");
@@ -638,6 +647,9 @@ void dap_destroy(dap_handle* h) {
     delete h->prof_state;
     if (h->d_inv_freq) (void)hipFree(h->d_inv_freq);
     if (h->d_err) (void)hipFree(h->d_err);
+    if (h->fork_ev) (void)hipEventDestroy(h->fork_ev);
+    if (h->join_ev) (void)hipEventDestroy(h->join_ev);
+    if (h->side) (void)hipStreamDestroy(h->side);
     delete h;
 }
 
@@ -758,19 +770,32 @@ int dap_step_paged(dap_handle* h, const uint16_t* q, const uint16_t* k, const ui
                       q_out, ld_q_out, k_pool, v_pool, n_pages, s);
     if (rc) return rc;
     const size_t dec_bytes = align256(dap_decode_workspace_bytes(h, n_step));
-    if (n_prompt > 0) {
+    // With both parts present (and outside validate mode, which synchronises
+    // per call), the prefill runs on the handle's second stream: its MFMA
+    // work overlaps the decode's HBM streaming. Fork after the write, join
+    // before returning, so the caller's stream orders everything as before.
+    const bool overlap = n_prompt > 0 && n_step > 0 && !h->validate;
+    hipStream_t ps = s;
+    if (overlap) {
+        hipError_t e = hipEventRecord(h->fork_ev, s);
+        if (e == hipSuccess) e = hipStreamWaitEvent(h->side, h->fork_ev, 0);
+        if (e != hipSuccess) return hip_fail(e, "forking the prefill stream");
+        ps = h->side;
+    }
+    if (n_prompt > 0)
         rc = do_prefill(h, q_out, ld_q_out, n_prompt, positions, rows, n_segments, table, table_ld, n_table_rows,
                         k_pool, v_pool, n_pages, out, ld_out, static_cast<char*>(workspace) + dec_bytes,
-                        workspace_bytes - dec_bytes, s);
-        if (rc) return rc;
-    }
-    if (n_step > 0) {
+                        workspace_bytes - dec_bytes, ps);
+    if (n_step > 0 && rc == DAP_OK)
         rc = do_decode(h, q_out + (int64_t)n_prompt * ld_q_out, ld_q_out, n_step, positions + n_prompt,
                        rows + n_prompt, table, table_ld, n_table_rows, k_pool, v_pool, n_pages,
                        out + (int64_t)n_prompt * ld_out, ld_out, workspace, dec_bytes, s);
-        if (rc) return rc;
+    if (overlap) {                                   // join even after an error: nothing outlives the call
+        hipError_t e = hipEventRecord(h->join_ev, h->side);
+        if (e == hipSuccess) e = hipStreamWaitEvent(s, h->join_ev, 0);
+        if (e != hipSuccess && rc == DAP_OK) return hip_fail(e, "joining the prefill stream");
     }
-    return DAP_OK;
+    return rc;
 }
 
 size_t dap_cache_workspace_bytes(const dap_handle* h, int32_t n_tokens, int32_t n_groups, int32_t cache_rows,

@@ -192,7 +192,12 @@ int dap_attn_decode_paged(dap_handle* handle,
  * the decode tokens. rows[t] is every token's table row (for prompt tokens
  * also its segment); positions, rows, slots (nullable) cover all tokens.
  * Runs the write over all tokens, then the packed prefill on the prompt
- * tokens and the decode on the step tokens, reading q from q_out.
+ * tokens and the decode on the step tokens, reading q from q_out. With both
+ * parts present the prefill runs on a second stream the handle owns (forked
+ * from and joined back to `stream` with events), so its matrix work overlaps
+ * the decode's memory streaming; the call still orders everything on
+ * `stream`. Calls on one handle must not be issued from several host threads
+ * at once (the fork and join events are the handle's).
  * out : [n_prompt + n_step][ld_out] bf16.
  * workspace : at least dap_step_workspace_bytes() bytes of scratch.
  */
