@@ -28,7 +28,7 @@ EXPORTS = ("dap_create", "dap_destroy", "dap_last_error", "dap_set_validate", "d
            "dap_decode_workspace_bytes", "dap_attn_decode_paged", "dap_step_workspace_bytes",
            "dap_step_paged", "dap_set_profiling", "dap_profile_read", "dap_cache_workspace_bytes",
            "dap_decode", "dap_decode_rows", "dap_prefill", "dap_prefill_slots", "dap_inpass_workspace_bytes",
-           "dap_packed", "dap_forward")
+           "dap_packed", "dap_forward", "dap_tile_layout")
 
 KERNELS = ("write", "prefill_tiles", "prefill", "decode", "decode_merge", "prep")
 
@@ -102,6 +102,7 @@ def load_library(path: str = LIB_PATH):
     lib.dap_inpass_workspace_bytes.restype = _SZ
     lib.dap_packed.argtypes = [_P, _P, _P, _P, _I64, _I32, _P, _P, _I32, _P, _P, _P, _I64, _P, _SZ, _P]
     lib.dap_forward.argtypes = [_P, _P, _P, _P, _I64, _I32, _I32, _P, _P, _P, _I64, _P, _SZ, _P]
+    lib.dap_tile_layout.argtypes = [_I32, _P, _P]
     lib.dap_set_profiling.argtypes = [_P, ctypes.c_int]
     lib.dap_profile_read.argtypes = [_P, ctypes.POINTER(ctypes.c_double), ctypes.POINTER(ctypes.c_int64),
                                      ctypes.c_int]
@@ -395,26 +396,64 @@ class Handle:
         return out
 
 
+_TILE_CACHE = {}
+
+
+def tile_offsets(head_dim: int, device="cpu"):
+    """Element offsets of logical K (key, d) and V (key, d) inside one page
+    tile, as two [64, D] int64 tensors, from the library (dap_tile_layout)."""
+    key = (head_dim, str(device))
+    if key not in _TILE_CACHE:
+        lib = load_library()
+        k = (ctypes.c_int32 * (64 * head_dim))()
+        v = (ctypes.c_int32 * (64 * head_dim))()
+        _check(lib.dap_tile_layout(head_dim, k, v))
+        kt = torch.tensor(list(k), dtype=torch.int64).view(64, head_dim)
+        vt = torch.tensor(list(v), dtype=torch.int64).view(64, head_dim)
+        _TILE_CACHE[key] = (kt.to(device), vt.to(device))
+    return _TILE_CACHE[key]
+
+
 def pools(n_pages: int, n_kv_heads: int, head_dim: int, device="cuda", dtype=torch.bfloat16):
-    """Empty K and V pools in the library's layout:
-    K [n_pages, Hkv, 64, D] (slot-major), V [n_pages, Hkv, D, 64] (dim-major)."""
-    k = torch.empty(n_pages, n_kv_heads, 64, head_dim, dtype=dtype, device=device)
-    v = torch.empty(n_pages, n_kv_heads, head_dim, 64, dtype=dtype, device=device)
+    """Empty K and V pools: [n_pages, Hkv, 64 * D] each, one tile per (page,
+    kv head) in the library's tile layout. Use store_pages / pool_logical /
+    gather_slots to move logical [.., 64, D] contents in and out."""
+    k = torch.empty(n_pages, n_kv_heads, 64 * head_dim, dtype=dtype, device=device)
+    v = torch.empty(n_pages, n_kv_heads, 64 * head_dim, dtype=dtype, device=device)
     return k, v
 
 
 def store_pages(k_pool, v_pool, page_ids, k_logical, v_logical):
-    """Place logical page contents [n, Hkv, 64, D] into the pools' layout
-    (V pages are stored dim-major)."""
+    """Place logical page contents [n, Hkv, 64, D] (key-major K and V) into
+    the pools' tile layout."""
+    n, hkv, _, D = k_logical.shape
+    koff, voff = tile_offsets(D, k_pool.device)
     idx = torch.as_tensor(page_ids, dtype=torch.long, device=k_pool.device)
-    k_pool[idx] = k_logical.view(k_pool.dtype)
-    v_pool[idx] = v_logical.view(v_pool.dtype).transpose(-1, -2)
+    kt = torch.empty(n, hkv, 64 * D, dtype=k_pool.dtype, device=k_pool.device)
+    vt = torch.empty_like(kt)
+    kt[:, :, koff.reshape(-1)] = k_logical.view(k_pool.dtype).reshape(n, hkv, 64 * D)
+    vt[:, :, voff.reshape(-1)] = v_logical.view(v_pool.dtype).reshape(n, hkv, 64 * D)
+    k_pool[idx] = kt
+    v_pool[idx] = vt
+
+
+def pool_logical(k_pool, v_pool, page_ids=None):
+    """Logical contents [n, Hkv, 64, D] of K and V pages (all pages if None)."""
+    D = k_pool.shape[-1] // 64
+    koff, voff = tile_offsets(D, k_pool.device)
+    kp = k_pool if page_ids is None else k_pool[torch.as_tensor(page_ids, dtype=torch.long, device=k_pool.device)]
+    vp = v_pool if page_ids is None else v_pool[torch.as_tensor(page_ids, dtype=torch.long, device=v_pool.device)]
+    n, hkv = kp.shape[0], kp.shape[1]
+    return (kp[:, :, koff.reshape(-1)].reshape(n, hkv, 64, D), vp[:, :, voff.reshape(-1)].reshape(n, hkv, 64, D))
 
 
 def gather_slots(k_pool, v_pool, slots):
     """Logical K and V at pool slots: two [T, Hkv, D] tensors."""
+    D = k_pool.shape[-1] // 64
+    koff, voff = tile_offsets(D, k_pool.device)
     s = torch.as_tensor(slots, dtype=torch.long, device=k_pool.device)
     pg, i = s // 64, s % 64
-    k = k_pool[pg, :, i, :]
-    v = v_pool[pg, :, :, i]
-    return k, v
+    hkv = k_pool.shape[1]
+    kidx = koff[i].unsqueeze(1).expand(len(s), hkv, D)
+    vidx = voff[i].unsqueeze(1).expand(len(s), hkv, D)
+    return torch.gather(k_pool[pg], 2, kidx), torch.gather(v_pool[pg], 2, vidx)

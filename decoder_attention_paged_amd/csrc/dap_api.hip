@@ -798,6 +798,17 @@ int dap_step_paged(dap_handle* h, const uint16_t* q, const uint16_t* k, const ui
     return rc;
 }
 
+int dap_tile_layout(int32_t head_dim, int32_t* k_offsets, int32_t* v_offsets) {
+    DAP_REQUIRE(head_dim == 64 || head_dim == 96 || head_dim == 128, DAP_UNSUPPORTED, "head_dim must be 64, 96 or 128");
+    DAP_REQUIRE(k_offsets && v_offsets, DAP_INVALID_ARG, "null argument");
+    for (int key = 0; key < dap::kPage; ++key)
+        for (int d = 0; d < head_dim; ++d) {
+            k_offsets[key * head_dim + d] = dap::k_tile_offset(key, d, head_dim);
+            v_offsets[key * head_dim + d] = dap::v_tile_offset(key, d, head_dim);
+        }
+    return DAP_OK;
+}
+
 size_t dap_cache_workspace_bytes(const dap_handle* h, int32_t n_tokens, int32_t n_groups, int32_t cache_rows,
                                  int32_t max_seq) {
     if (!h || n_tokens < 0 || n_groups < 0 || cache_rows < 0 || max_seq <= 0 || max_seq % dap::kPage) return 0;

@@ -24,6 +24,45 @@ enum ErrorBits : unsigned {
     kErrSpan = 64u,      // an in-pass segment's positions do not fit its scratch pages
 };
 
+// ---- page tile layout ------------------------------------------------------
+// A (page, kv head) tile of 64 keys x D dims is stored as 16-byte chunks (8
+// bf16) in the order one decode wave loads them, 64 lanes x 16 bytes = 1 KB
+// per load, so every load reads one contiguous kilobyte.
+// K: fragment f = (half * 2 + blk) * (D / 32) + s, lane l = 16 * grp + i holds
+//    key 32 * half + unit_key(blk, i), dims 32 * s + 8 * grp .. + 7.
+// V: fragment f = half * (D / 16) + db, lane l = 16 * grp + col holds dim
+//    16 * db + col, keys 32 * half + 8 * grp .. + 7.
+// unit_key permutes the keys of a 32-key half inside the 16x16 S blocks so
+// that lane group g's S values are the 8 contiguous keys its V chunk holds.
+__host__ __device__ __forceinline__ int unit_key(int blk, int i) { return 8 * (i >> 2) + 4 * blk + (i & 3); }
+
+// element offset of K (key, d) / V (key, d) inside a tile
+__host__ __device__ __forceinline__ int k_tile_offset(int key, int d, int D) {
+    const int half = key >> 5, kk = key & 31;
+    const int blk = (kk >> 2) & 1, i = ((kk >> 3) << 2) | (kk & 3);
+    const int f = (half * 2 + blk) * (D / 32) + (d >> 5);
+    return ((f * 64 + ((d >> 3) & 3) * 16 + i) << 3) + (d & 7);
+}
+__host__ __device__ __forceinline__ int v_tile_offset(int key, int d, int D) {
+    const int half = key >> 5, kk = key & 31;
+    const int f = half * (D / 16) + (d >> 4);
+    return ((f * 64 + (kk >> 3) * 16 + (d & 15)) << 3) + (kk & 7);
+}
+// the 8 elements of 16-byte chunk c: K row `key` dims d0..d0+7; V dim `d`
+// keys key0..key0+7
+__host__ __device__ __forceinline__ void k_tile_chunk(int c, int D, int& key, int& d0) {
+    const int f = c >> 6, l = c & 63;
+    const int hb = f / (D / 32), s = f % (D / 32);
+    key = 32 * (hb >> 1) + unit_key(hb & 1, l & 15);
+    d0 = 32 * s + 8 * (l >> 4);
+}
+__host__ __device__ __forceinline__ void v_tile_chunk(int c, int D, int& d, int& key0) {
+    const int f = c >> 6, l = c & 63;
+    const int half = f / (D / 16), db = f % (D / 16);
+    d = 16 * db + (l & 15);
+    key0 = 32 * half + 8 * (l >> 4);
+}
+
 typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
 typedef float f32x4 __attribute__((ext_vector_type(4)));
 typedef float f32x16 __attribute__((ext_vector_type(16)));

@@ -12,8 +12,8 @@
 // the N columns of 16x16x32 bf16 MFMAs: S[key][head] = K q^T and
 // O^T[dim][head] += V^T P^T, so a page's K and V are read from HBM once for
 // all g heads and the VALU only runs the softmax. A page tile is one
-// contiguous block per kv head (K slot-major, V dim-major), and every lane
-// reads 16 contiguous bytes per load.
+// contiguous block per kv head, stored in the order the waves load it, so
+// every load of a wave reads one contiguous kilobyte.
 //
 // Merge: a row whose range fits one chunk is finished by that workgroup.
 // Otherwise each chunk stores its fp32 (m, l, o) per head in the workspace
@@ -31,12 +31,12 @@ constexpr float kLog2e = 1.4426950408889634f;
 
 __device__ __forceinline__ bf16x8 as_bf16x8(u32x4 u) { return __builtin_bit_cast(bf16x8, u); }
 
-// A wave works on 32-key units (half pages). In a unit, S block blk (16
-// keys) holds in A-row i the key 8*(i/4) + 4*blk + i%4, so lane group g ends
-// up with the S values of keys 8g .. 8g+7, which are the 8 contiguous keys
-// its V^T fragment covers in the PV step; K and V^T loads both read 64
-// contiguous bytes per row per instruction.
-__device__ __forceinline__ int unit_key(int blk, int i) { return 8 * (i >> 2) + 4 * blk + (i & 3); }
+// A wave works on 32-key units (half pages): two 16-key S blocks and the
+// V^T of the same 32 keys. The tile layout (dap_internal.h) stores each of
+// the unit's K and V fragments as the 1 KB one load of the wave reads, lane
+// by lane, with unit_key placing in lane group g's S values the 8 contiguous
+// keys its V fragment covers. The loads are non-temporal: the tiles are read
+// once per call, and contiguous kilobytes read that way stream fastest.
 
 constexpr int kMaxPagesPerSplit = 256;
 constexpr int kMaxSplits = 256;          // chunks per row (pps >= 4 caps this for max_position <= 65536)
@@ -47,26 +47,18 @@ struct UnitFrags {
     u32x4 v[D / 16];      // V^T, 16 dims x 32 keys per block
 };
 
-// Per-lane element offsets inside a page tile, fixed for the whole kernel:
-// K rows of the two 16-key blocks at dims 8*grp + 32s, V^T rows 16db + col.
-template <int D>
-struct LaneOffsets {
-    int k[2];    // + 32 * half * D selects the half page
-    int v;       // + 32 * half, + 16 * db * kPage per dim block
-};
-
 template <int D>
 __device__ __forceinline__ void load_unit(UnitFrags<D>& f, const uint16_t* kt, const uint16_t* vt, int half,
-                                          const LaneOffsets<D>& lo) {
+                                          int lane) {
+    const u32x4* kb = reinterpret_cast<const u32x4*>(kt) + lane;
 #pragma unroll
-    for (int blk = 0; blk < 2; ++blk) {
-        const uint16_t* kr = kt + lo.k[blk] + 32 * half * D;
+    for (int blk = 0; blk < 2; ++blk)
 #pragma unroll
-        for (int s = 0; s < D / 32; ++s) f.k[blk][s] = *reinterpret_cast<const u32x4*>(kr + 32 * s);
-    }
-    const uint16_t* vr = vt + lo.v + 32 * half;
+        for (int s = 0; s < D / 32; ++s)
+            f.k[blk][s] = __builtin_nontemporal_load(kb + ((half * 2 + blk) * (D / 32) + s) * 64);
+    const u32x4* vb = reinterpret_cast<const u32x4*>(vt) + lane;
 #pragma unroll
-    for (int db = 0; db < D / 16; ++db) f.v[db] = *reinterpret_cast<const u32x4*>(vr + 16 * db * kPage);
+    for (int db = 0; db < D / 16; ++db) f.v[db] = __builtin_nontemporal_load(vb + (half * (D / 16) + db) * 64);
 }
 
 struct RowRange {
@@ -234,10 +226,6 @@ __global__ __launch_bounds__(kDecodeThreads, 2) void decode_kernel(AttnArgs a, i
     // loads in flight is the same on every path and the wait before the
     // compute covers only the current unit.
     const int n_units = 2 * n_local;
-    LaneOffsets<D> lofs;
-    lofs.k[0] = unit_key(0, col) * D + 8 * grp;
-    lofs.k[1] = unit_key(1, col) * D + 8 * grp;
-    lofs.v = col * kPage + 8 * grp;
     auto prep = [&](int u, int& base, const uint16_t*& kt, const uint16_t*& vt, int& half) -> bool {
         kt = a.k_pool;
         vt = a.v_pool;
@@ -256,15 +244,15 @@ __global__ __launch_bounds__(kDecodeThreads, 2) void decode_kernel(AttnArgs a, i
     const uint16_t *kt, *vt;
     int u = wave;
     bool ok_a = prep(u, base_a, kt, vt, half);
-    load_unit<D>(fa, kt, vt, half, lofs);
+    load_unit<D>(fa, kt, vt, half, lane);
     while (u < n_units) {
         const bool ok_b = prep(u + kDecodeWaves, base_b, kt, vt, half);
-        load_unit<D>(fb, kt, vt, half, lofs);
+        load_unit<D>(fb, kt, vt, half, lane);
         if (ok_a) compute_unit<D>(st, fa, qf, c, base_a, rr.lo, rr.p, grp);
         u += kDecodeWaves;
         if (u >= n_units) break;
         ok_a = prep(u + kDecodeWaves, base_a, kt, vt, half);
-        load_unit<D>(fa, kt, vt, half, lofs);
+        load_unit<D>(fa, kt, vt, half, lane);
         if (ok_b) compute_unit<D>(st, fb, qf, c, base_b, rr.lo, rr.p, grp);
         u += kDecodeWaves;
     }

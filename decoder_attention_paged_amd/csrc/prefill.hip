@@ -12,7 +12,7 @@
 // one (tile, kv head): wave w owns 32 query rows = one of the g query heads
 // sharing the kv head, for 32 of the tile's tokens, so each K/V page tile is
 // read from memory once per workgroup for all g heads and 256 query rows.
-// Per 64-key page the workgroup stages K (slot-major) and V^T (dim-major)
+// Per 64-key page the workgroup stages K (key-major) and V^T (dim-major)
 // into one of two LDS buffers (one barrier per page), and each
 // wave computes S^T = K Q^T and O^T += V^T P^T with 32x32x16 bf16 MFMAs and
 // an online softmax in float32 (exp2 with the scale folded in, O rescaled
@@ -232,10 +232,11 @@ __global__ __launch_bounds__(kPrefillThreads) void prefill_kernel(AttnArgs a, co
         for (int i = 0; i < kChunks; ++i) {
             const int cidx = tid + kPrefillThreads * i;
             if (kTileChunks % kPrefillThreads == 0 || cidx < kTileChunks) {
-                const int kr = cidx / (D / 8), kc = cidx % (D / 8);
-                *reinterpret_cast<u32x4*>(&sk[kr * KS + 8 * kc]) = pk[i];
-                const int vr = cidx / (kPage / 8), vc = cidx % (kPage / 8);
-                *reinterpret_cast<u32x4*>(&sv[vr * VS + 8 * vc]) = pv[i];
+                int key, d0, d, key0;                 // the chunk's place in the tile layout
+                k_tile_chunk(cidx, D, key, d0);
+                *reinterpret_cast<u32x4*>(&sk[key * KS + d0]) = pk[i];
+                v_tile_chunk(cidx, D, d, key0);
+                *reinterpret_cast<u32x4*>(&sv[d * VS + key0]) = pv[i];
             }
         }
     };

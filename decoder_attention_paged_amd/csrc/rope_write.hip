@@ -4,8 +4,11 @@
 // and their sine/cosine are computed once in float64 into LDS, then every q
 // and k head of the token is normed (optionally), rotated and rounded to
 // bf16 once. In the same launch, one workgroup per (64 tokens, kv head)
-// copies v into the dim-major V tiles through an LDS transpose, so a page's
-// consecutive slots are written as contiguous runs. This is a bandwidth-bound pass (a few flops per byte), so the
+// copies v into the V tiles through an LDS transpose, so the consecutive
+// slots of one dim are written as contiguous runs (the tile layout keeps 8
+// consecutive keys of a dim together). Page tiles are in the library's
+// tile layout, 16-byte chunks in the order the decode loads them. This is a
+// bandwidth-bound pass (a few flops per byte), so the
 // float64 arithmetic costs nothing and lets K pages match the float64
 // definition bit for bit up to a final rounding tie.
 //
@@ -59,7 +62,7 @@ __device__ __forceinline__ long long token_slot(const WriteArgs& a, int t, int p
 
 // V of kVTile consecutive tokens, per kv head: rows read coalesced, turned
 // around in LDS, and stored with lanes running along tokens, so the tokens
-// of one page land as contiguous runs of each dim-major V row.
+// of one page land as contiguous runs of 8 keys per dim.
 template <int D>
 __device__ __forceinline__ void write_v_tile(const WriteArgs& a, int t0, int kh) {
     constexpr int VS = kVTile + 2;     // LDS row stride (elements), odd word stride
@@ -84,8 +87,8 @@ __device__ __forceinline__ void write_v_tile(const WriteArgs& a, int t0, int kh)
             const int d = e / kVTile, tt = e % kVTile;
             const long long slot = s_slot[tt];
             if (tt >= n || slot < 0) continue;
-            a.v_pool[(((slot >> 6) * a.n_kv_heads + kh) * D + d) * (long long)kPage + (slot & (kPage - 1))] =
-                s_v[d * VS + tt];
+            a.v_pool[((slot >> 6) * a.n_kv_heads + kh) * (long long)(D * kPage) +
+                     v_tile_offset((int)(slot & (kPage - 1)), d, D)] = s_v[d * VS + tt];
         }
     }
 }
@@ -199,7 +202,10 @@ __global__ __launch_bounds__(kWriteThreads) void rope_write_kernel(WriteArgs a, 
         } else {
             if (slot < 0) continue;
             const int kh = head - a.n_q_heads;
-            dst = a.k_pool + ((page * a.n_kv_heads + kh) * kPage + in_page) * (long long)D;
+            uint16_t* tile = a.k_pool + (page * a.n_kv_heads + kh) * (long long)(D * kPage);
+            *reinterpret_cast<u32x4*>(tile + k_tile_offset(in_page, 8 * j, D)) = ol;
+            *reinterpret_cast<u32x4*>(tile + k_tile_offset(in_page, kHalf + 8 * j, D)) = oh;
+            continue;
         }
         *reinterpret_cast<u32x4*>(dst + 8 * j) = ol;
         *reinterpret_cast<u32x4*>(dst + kHalf + 8 * j) = oh;

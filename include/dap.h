@@ -29,8 +29,11 @@
  *    DAP_BAD_INDEX.
  *
  * Page pool layout (bf16), n_pages pages of 64 positions each:
- *   K pool [n_pages][n_kv_heads][64][head_dim]   slot-major page tiles
- *   V pool [n_pages][n_kv_heads][head_dim][64]   dim-major page tiles
+ *   K pool [n_pages][n_kv_heads][64 * head_dim]   one tile per (page, kv head)
+ *   V pool [n_pages][n_kv_heads][64 * head_dim]
+ * Inside a tile, K[key][d] and V[key][d] sit where dap_tile_layout says:
+ * 16-byte chunks (8 dims of one key for K, 8 keys of one dim for V) in the
+ * order the decode's waves load them, one contiguous kilobyte per load.
  * Position j of table row r lives in page table[r*table_ld + j/64] at index
  * j%64; its slot number is page*64 + j%64. (The pages: "Mistral 7B Instruct
  * v0.3", Entries table, decode_paged: a pool of positions in pages of
@@ -213,6 +216,22 @@ int dap_step_paged(dap_handle* handle,
     uint16_t* k_pool, uint16_t* v_pool, int32_t n_pages,
     uint16_t* out, int64_t ld_out,
     void* workspace, size_t workspace_bytes, void* stream);
+
+/*
+ * Page tile layout (host only; no device call). Fills, for head_dim D,
+ * k_offsets[key * D + d] and v_offsets[key * D + d] (64 * D entries each)
+ * with the element offset of logical K[key][d] and V[key][d] inside one
+ * (page, kv head) tile. Tiles hold 64 * D bf16 each, 16-byte chunks of 8
+ * elements in the order the decode's waves load them (one kilobyte, 64
+ * lanes x 16 bytes, per load):
+ *   K chunk f*64 + l, f = (h*2 + b)*(D/32) + s, l = 16*g + i:
+ *     key 32*h + u(b, i), dims 32*s + 8*g .. +7;
+ *   V chunk f*64 + l, f = h*(D/16) + e, l = 16*g + c:
+ *     dim 16*e + c, keys 32*h + 8*g .. +7;
+ * with u(b, i) = 8*(i/4) + 4*b + i%4. Returns DAP_UNSUPPORTED for D not in
+ * {64, 96, 128}.
+ */
+int dap_tile_layout(int32_t head_dim, int32_t* k_offsets, int32_t* v_offsets);
 
 /*
  * Contiguous-cache entries.

@@ -62,3 +62,34 @@ def test_null_handle_is_rejected():
     assert lib.dap_decode_workspace_bytes(None, 4) == 0
     assert lib.dap_attn_decode_paged(None, None, 0, 1, None, None, None, 1, 1, None, None, 1, None, 0,
                                      None, 0, None) == dap.INVALID_ARG
+
+
+@pytest.mark.parametrize("head_dim", [64, 96, 128])
+def test_tile_layout_is_a_permutation_of_16_byte_chunks(head_dim):
+    """dap_tile_layout (host only) maps each logical element to a distinct
+    tile offset; every 8-element chunk of a K row (dims 8c..8c+7) and of a V
+    dim (keys 8c..8c+7) is contiguous; the binding's pool helpers round-trip."""
+    import torch
+    D = head_dim
+    ko, vo = dap.tile_offsets(D)
+    for off in (ko, vo):
+        assert sorted(off.reshape(-1).tolist()) == list(range(64 * D))
+    for c in range(D // 8):
+        run = ko[:, 8 * c:8 * c + 8]
+        assert torch.equal(run - run[:, :1], torch.arange(8).expand(64, 8))
+    for c in range(8):
+        run = vo[8 * c:8 * c + 8, :].t()
+        assert torch.equal(run - run[:, :1], torch.arange(8).expand(D, 8))
+    # one kilobyte = one decode load: K chunk 0..63 are keys unit_key(0, i) at dims 0..31
+    keys = [8 * (i >> 2) + (i & 3) for i in range(16)]
+    first = sorted(int(ko[k, 8 * g]) for g in range(4) for k in keys)
+    assert first == list(range(0, 512, 8))
+    kp, vp = dap.pools(3, 2, D, device="cpu")
+    kl = torch.randint(0, 16000, (2, 2, 64, D), dtype=torch.int16)
+    vl = torch.randint(0, 16000, (2, 2, 64, D), dtype=torch.int16)
+    dap.store_pages(kp, vp, [2, 0], kl, vl)
+    k2, v2 = dap.pool_logical(kp, vp, [2, 0])
+    assert torch.equal(k2.view(torch.int16), kl) and torch.equal(v2.view(torch.int16), vl)
+    kg, vg = dap.gather_slots(kp, vp, torch.tensor([2 * 64 + 7, 63]))
+    assert torch.equal(kg.view(torch.int16), torch.stack([kl[0, :, 7], kl[1, :, 63]]))
+    assert torch.equal(vg.view(torch.int16), torch.stack([vl[0, :, 7], vl[1, :, 63]]))

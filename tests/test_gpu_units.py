@@ -173,10 +173,12 @@ def test_write_matches_oracle_bits(model, explicit_slots):
     assert np.array_equal(to_np_bits(vg), v_bits), "V pages must be a bit copy"
     # nothing else in the pools changed
     s = torch.as_tensor(slots, device="cuda")
-    k_before[s // 64, :, s % 64, :] = kp[s // 64, :, s % 64, :]
-    v_before[s // 64, :, :, s % 64] = vp[s // 64, :, :, s % 64]
-    assert torch.equal(k_before.view(torch.int16), kp.view(torch.int16))
-    assert torch.equal(v_before.view(torch.int16), vp.view(torch.int16))
+    kb, vb = dap.pool_logical(k_before, v_before)
+    ka, va = dap.pool_logical(kp, vp)
+    kb[s // 64, :, s % 64, :] = ka[s // 64, :, s % 64, :]
+    vb[s // 64, :, s % 64, :] = va[s // 64, :, s % 64, :]
+    assert torch.equal(kb.view(torch.int16), ka.view(torch.int16))
+    assert torch.equal(vb.view(torch.int16), va.view(torch.int16))
 
 
 def test_write_in_place_q():
