@@ -86,7 +86,7 @@ class Bench:
 
     def __init__(self, name):
         self.name = name
-        self.wl = W.ALL[name]()
+        self.wl = W.ALL["phi3" if name == "phi3_loop" else name]()
         wl, m = self.wl, self.wl.model
         self.m = m
         self.h = dap.Handle(dap.Model(m.n_q_heads, m.n_kv_heads, m.head_dim, m.rope_theta, window=m.window,
@@ -158,6 +158,46 @@ class Bench:
             self.tokens = T + 4
             self.desc = ("phi-3-mini-shaped: prefill_packed of 4096 tokens (prompts 512/1024/1536/1024, window "
                          "2047, Hq=Hkv=32, D96) then decode_paged of the 4 rows at position 3000")
+        elif name == "phi3_loop":
+            # the prompts are prefilled once; a step is the whole decode loop
+            T = wl.n_pre
+            qkv = wl.qkv("prompt", T, "cuda")
+            pos, seg = i32(wl.pre_positions), i32(wl.pre_segments)
+            pq = self.h.rope_qknorm_write_pages(qkv[:, :hq * D], qkv[:, hq * D:(hq + hkv) * D],
+                                                qkv[:, (hq + hkv) * D:], pos, self.kp, self.vp, rows=seg,
+                                                table=self.table)
+            self.h.attn_prefill_packed(pq, pos, seg, self.table, self.kp, self.vp, n_segments=4)
+            self.loop = []
+            self.dec_bytes = 0
+            n_tok = 0
+            for t, (rows, positions) in enumerate(W.phi3_decode_schedule()):
+                x = wl.qkv("step", len(rows), "cuda", row0=4 * t)
+                self.loop.append((x, i32(positions), i32(rows),
+                                  torch.empty(len(rows), hq * D, dtype=torch.int16, device="cuda"),
+                                  torch.empty(len(rows), hq * D, dtype=torch.int16, device="cuda")))
+                self.dec_bytes += decode_bytes(m, positions)
+                n_tok += len(rows)
+            self.ws = self.h.workspace(self.h.decode_workspace_bytes(4))
+            self.bytes = write_bytes(m, n_tok) + self.dec_bytes
+            self.flops = 0.0
+            self.tokens = n_tok
+            self.qkv = qkv
+            self.desc = ("phi-3-mini-shaped decode loop: 2489 steps (7908 row-steps) from each prompt end to position "
+                         "3000, window 2047, Hq=Hkv=32, D96; a write and a decode per step, the loop captured as one "
+                         "HIP graph and replayed")
+            torch.cuda.synchronize()
+            self.step_eager()
+            torch.cuda.synchronize()
+            self.graph = torch.cuda.CUDAGraph()
+            side = torch.cuda.Stream()
+            side.wait_stream(torch.cuda.current_stream())
+            with torch.cuda.stream(side):
+                self.step_eager()
+            torch.cuda.current_stream().wait_stream(side)
+            torch.cuda.synchronize()
+            with torch.cuda.graph(self.graph):
+                self.step_eager()
+            torch.cuda.synchronize()
         elif name == "mistral_contiguous":
             R = wl.n_dec
             self.qkv = wl.qkv("step", R, "cuda")
@@ -191,7 +231,21 @@ class Bench:
         torch.cuda.synchronize()
 
     def step(self):
+        if self.name == "phi3_loop":
+            self.graph.replay()
+            return
+        self.step_eager()
+
+    def step_eager(self):
         h, m, wl = self.h, self.m, self.wl
+        if self.name == "phi3_loop":
+            for x, tp, tr, qo, o in self.loop:
+                h.rope_qknorm_write_pages(x[:, :m.n_q_heads * m.head_dim],
+                                          x[:, m.n_q_heads * m.head_dim:(m.n_q_heads + m.n_kv_heads) * m.head_dim],
+                                          x[:, (m.n_q_heads + m.n_kv_heads) * m.head_dim:], tp, self.kp, self.vp,
+                                          rows=tr, table=self.table, q_out=qo)
+                h.attn_decode_paged(qo, tp, self.table, self.kp, self.vp, rows=tr, out=o, workspace=self.ws)
+            return
         if self.name == "qwen3":
             h.step_paged(*self.split, self.pos, self.rows, self.table, self.kp, self.vp, n_prompt=wl.n_pre,
                          n_segments=8, q_gain=self.gains[0], k_gain=self.gains[1], q_out=self.q_out, out=self.out,
@@ -240,6 +294,8 @@ def cpu_baseline(b: Bench, budget_s: float = 20.0):
         dec_pick = np.arange(wl.n_dec)
     elif b.name == "packed_train":
         return cpu_baseline_inpass(b, freqs, threads)
+    elif b.name == "phi3_loop":
+        return cpu_baseline_loop(b, freqs, threads)
     elif b.name in ("mistral", "mistral_contiguous"):
         tok_pos, tok_rows = wl.dec_positions, wl.dec_rows
         pre_pick = np.zeros(0, int)
@@ -328,6 +384,37 @@ def cpu_baseline_inpass(b: Bench, freqs, threads):
             "sample": sample, "seconds": round(dt, 2)}
 
 
+def cpu_baseline_loop(b: Bench, freqs, threads):
+    """The oracle on every 20th step of the Phi-3 decode loop: the front half
+    of the step's tokens and each row's attention over its window (pages as
+    generated; the cost is what is timed)."""
+    from oracle import attention, bf16, core
+
+    wl, m = b.wl, b.m
+    steps = W.phi3_decode_schedule()[::20]
+    need = set()
+    for rows, positions in steps:
+        for r, p in zip(rows, positions):
+            need.update(int(x) for x in wl.table[r, max(0, p - m.window + 1) // 64: p // 64 + 1])
+    cache = {}
+    need = sorted(need)
+    k = wl.pages("k", need, "cuda").cpu().numpy().view(np.uint16)
+    v = wl.pages("v", need, "cuda").cpu().numpy().view(np.uint16)
+    for j, pg in enumerate(need):
+        cache[pg] = (bf16.to_f64(k[j]), bf16.to_f64(v[j]))
+    t0 = time.perf_counter()
+    done = 0
+    for i, (rows, positions) in enumerate(steps):
+        x = wl.qkv("step", len(rows), "cpu", row0=4 * 20 * i).numpy().view(np.uint16)
+        q, _, _ = core.prepare_tokens(x, positions, m.n_q_heads, m.n_kv_heads, m.head_dim, freqs)
+        attention.paged(bf16.round_f64(q), positions, rows, wl.table, lambda pg: cache[pg], m.window)
+        done += write_bytes(m, len(rows)) + decode_bytes(m, positions)
+    dt = time.perf_counter() - t0
+    return {"value": round(done / dt / 1e9, 4), "unit": "GB/s", "cores": int(threads), "kind": "oracle",
+            "sample": f"every 20th step of the decode loop ({len(steps)} steps): front half and attention; "
+                      f"{done / 1e9:.3f} GB of algorithmic traffic in {dt:.1f} s", "seconds": round(dt, 2)}
+
+
 # --------------------------------------------------------------------------- copy ceiling
 def copy_ceiling(nbytes: int = 1 << 30, reps: int = 10) -> float:
     """Measured device-to-device copy rate (bytes read + bytes written per
@@ -372,7 +459,8 @@ def main():
     ap.add_argument("--steps", type=int, default=20)
     ap.add_argument("--warmup", type=int, default=3)
     ap.add_argument("--workload", default="qwen3",
-                    choices=["qwen3", "mistral", "llama31", "phi3", "mistral_contiguous", "packed_train"])
+                    choices=["qwen3", "mistral", "llama31", "phi3", "phi3_loop", "mistral_contiguous",
+                             "packed_train"])
     ap.add_argument("--no-cpu-baseline", action="store_true")
     args = ap.parse_args()
     if args.gpus != 1:
@@ -407,7 +495,7 @@ def main():
     marks = [torch.cuda.Event(enable_timing=True) for _ in range(args.steps + 1)]
     marks[0].record()
     for i in range(args.steps):
-        b.step()
+        b.step_eager()
         marks[i + 1].record()
     torch.cuda.synchronize()
     prof = b.h.profile_read(reset=True)
@@ -418,20 +506,26 @@ def main():
     m = b.m
     value = b.bytes / (ms_per_step * 1e-3) / 1e9
     dom = max(("decode", "prefill", "write"), key=lambda k: prof[k][0])
+    # totals over the profiled pass (args.steps steps; a step may hold many launches)
+    total_ms = {k: v[0] for k, v in prof.items()}
+    launches = {k: max(v[1], 1) for k, v in prof.items()}
     if dom == "decode":
-        per_launch = b.dec_bytes
-        achieved = per_launch / (kern_ms["decode"] * 1e-3) / 1e9
+        total = b.dec_bytes * args.steps
+        achieved = total / (total_ms["decode"] * 1e-3) / 1e9
         roof = {"bound": "hbm", "achieved": round(achieved, 2), "peak": HBM_PEAK_GBS, "unit": "GB/s",
                 "frac": round(achieved / HBM_PEAK_GBS, 4), "kernel": "decode_kernel",
-                "avg_launch_ms": round(kern_ms["decode"], 5), "algorithmic_bytes_per_launch": per_launch}
+                "avg_launch_ms": round(kern_ms["decode"], 5),
+                "algorithmic_bytes_per_launch": int(total // launches["decode"])}
     elif dom == "prefill":
-        achieved = b.flops / (kern_ms["prefill"] * 1e-3) / 1e12
+        total = b.flops * args.steps
+        achieved = total / (total_ms["prefill"] * 1e-3) / 1e12
         roof = {"bound": "mfma", "achieved": round(achieved, 2), "peak": BF16_PEAK_TFLOPS, "unit": "TFLOP/s",
                 "frac": round(achieved / BF16_PEAK_TFLOPS, 4), "kernel": "prefill_kernel",
-                "avg_launch_ms": round(kern_ms["prefill"], 5), "algorithmic_flops_per_launch": b.flops}
+                "avg_launch_ms": round(kern_ms["prefill"], 5),
+                "algorithmic_flops_per_launch": total / launches["prefill"]}
     else:
-        per_launch = write_bytes(m, b.tokens)
-        achieved = per_launch / (kern_ms["write"] * 1e-3) / 1e9
+        total = write_bytes(m, b.tokens) * args.steps
+        achieved = total / (total_ms["write"] * 1e-3) / 1e9
         roof = {"bound": "hbm", "achieved": round(achieved, 2), "peak": HBM_PEAK_GBS, "unit": "GB/s",
                 "frac": round(achieved / HBM_PEAK_GBS, 4), "kernel": "rope_write_kernel",
                 "avg_launch_ms": round(kern_ms["write"], 5)}
@@ -455,10 +549,10 @@ def main():
         # event span covers the overlap, so it is no measure of the kernel's rate
         line["prefill_overlaps_decode"] = True
     elif b.flops:
-        line["prefill_tflops"] = round(b.flops / (kern_ms["prefill"] * 1e-3) / 1e12, 2)
+        line["prefill_tflops"] = round(b.flops * args.steps / (total_ms["prefill"] * 1e-3) / 1e12, 2)
         line["prefill_frac_of_mfma_peak"] = round(line["prefill_tflops"] / BF16_PEAK_TFLOPS, 4)
     if b.dec_bytes:
-        g = b.dec_bytes / (kern_ms["decode"] * 1e-3) / 1e9
+        g = b.dec_bytes * args.steps / (total_ms["decode"] * 1e-3) / 1e9
         line["decode_gbps"] = round(g, 2)
         line["decode_frac_of_hbm_peak"] = round(g / HBM_PEAK_GBS, 4)
     if not args.no_cpu_baseline:

@@ -93,6 +93,93 @@ __device__ __forceinline__ void write_v_tile(const WriteArgs& a, int t0, int kh)
     }
 }
 
+// One q or k head chunk pair of token t: lanes 8h..8h+7 of a head hold its
+// dims 8j..8j+7 and D/2+8j..D/2+8j+7 (rlo, rhi, raw bf16). Norm (the head's
+// sum of squares over its 8 lanes), rotate by the token's angles (cs, sn in
+// LDS), round once to bf16, store to q_out or the K tile. Every lane of the
+// wave calls it (the shuffles are wave-wide); inactive lanes store nothing.
+template <int D>
+__device__ __forceinline__ void rope_item(const WriteArgs& a, int t, int head, int j, bool active, u32x4 rlo,
+                                          u32x4 rhi, const double* cs, const double* sn, long long slot) {
+    constexpr int kHalf = D / 2;
+    const bool is_q = head < a.n_q_heads;
+    double xl[8], xh[8];
+#pragma unroll
+    for (int w = 0; w < 4; ++w) {
+        xl[2 * w] = (double)bf16_to_f32(rlo[w] & 0xffffu);
+        xl[2 * w + 1] = (double)bf16_to_f32(rlo[w] >> 16);
+        xh[2 * w] = (double)bf16_to_f32(rhi[w] & 0xffffu);
+        xh[2 * w + 1] = (double)bf16_to_f32(rhi[w] >> 16);
+    }
+    if (a.qk_norm) {
+        double ss = 0.0;
+#pragma unroll
+        for (int i = 0; i < 8; ++i) ss += xl[i] * xl[i] + xh[i] * xh[i];
+        ss += __shfl_xor(ss, 1);
+        ss += __shfl_xor(ss, 2);
+        ss += __shfl_xor(ss, 4);
+        if (active) {
+            const double denom = sqrt(ss / (double)D + a.eps);
+            const uint16_t* g = is_q ? a.q_gain : a.k_gain;
+            const u32x4 gl = *reinterpret_cast<const u32x4*>(g + 8 * j);
+            const u32x4 gh = *reinterpret_cast<const u32x4*>(g + kHalf + 8 * j);
+#pragma unroll
+            for (int w = 0; w < 4; ++w) {
+                xl[2 * w] = (double)bf16_to_f32(gl[w] & 0xffffu) * xl[2 * w] / denom;
+                xl[2 * w + 1] = (double)bf16_to_f32(gl[w] >> 16) * xl[2 * w + 1] / denom;
+                xh[2 * w] = (double)bf16_to_f32(gh[w] & 0xffffu) * xh[2 * w] / denom;
+                xh[2 * w + 1] = (double)bf16_to_f32(gh[w] >> 16) * xh[2 * w + 1] / denom;
+            }
+        }
+    }
+    if (!active) return;
+    u32x4 ol, oh;
+#pragma unroll
+    for (int w = 0; w < 4; ++w) {
+        uint32_t l2[2], h2[2];
+#pragma unroll
+        for (int e = 0; e < 2; ++e) {
+            const int i = 2 * w + e;
+            const double c = cs[8 * j + i];
+            const double s = sn[8 * j + i];
+            l2[e] = f64_to_bf16(xl[i] * c - xh[i] * s);
+            h2[e] = f64_to_bf16(xh[i] * c + xl[i] * s);
+        }
+        ol[w] = l2[0] | (l2[1] << 16);
+        oh[w] = h2[0] | (h2[1] << 16);
+    }
+    if (is_q) {
+        uint16_t* dst = a.q_out + (long long)t * a.ld_q_out + (long long)head * D;
+        *reinterpret_cast<u32x4*>(dst + 8 * j) = ol;
+        *reinterpret_cast<u32x4*>(dst + kHalf + 8 * j) = oh;
+        return;
+    }
+    if (slot < 0) return;
+    const int kh = head - a.n_q_heads;
+    const int in_page = (int)(slot & (kPage - 1));
+    uint16_t* tile = a.k_pool + ((slot >> 6) * a.n_kv_heads + kh) * (long long)(D * kPage);
+    *reinterpret_cast<u32x4*>(tile + k_tile_offset(in_page, 8 * j, D)) = ol;
+    *reinterpret_cast<u32x4*>(tile + k_tile_offset(in_page, kHalf + 8 * j, D)) = oh;
+}
+
+// raw rows of item `item` (8 lanes per head) of token t, zeros past the heads
+template <int D>
+__device__ __forceinline__ void load_item(const WriteArgs& a, int t, int item, int n_rope_heads, u32x4& lo,
+                                          u32x4& hi, int& head, int& j, bool& active) {
+    head = item / kLanesPerHead;
+    j = item % kLanesPerHead;
+    active = head < n_rope_heads && j < D / 16;
+    lo = u32x4{0u, 0u, 0u, 0u};
+    hi = lo;
+    if (active) {
+        const uint16_t* src = head < a.n_q_heads ? a.q + (long long)t * a.ld_in + (long long)head * D
+                                                 : a.k + (long long)t * a.ld_in + (long long)(head - a.n_q_heads) * D;
+        lo = *reinterpret_cast<const u32x4*>(src + 8 * j);
+        hi = *reinterpret_cast<const u32x4*>(src + D / 2 + 8 * j);
+    }
+}
+
+// Many tokens: one wave per token, four tokens per workgroup.
 template <int D>
 __global__ __launch_bounds__(kWriteThreads) void rope_write_kernel(WriteArgs a, int n_vtiles) {
     if ((int)blockIdx.x < n_vtiles * a.n_kv_heads) {  // uniform per workgroup
@@ -101,7 +188,6 @@ __global__ __launch_bounds__(kWriteThreads) void rope_write_kernel(WriteArgs a, 
     }
     static_assert(D % 16 == 0 && D / 16 <= kLanesPerHead, "head_dim");
     constexpr int kHalf = D / 2;
-    constexpr int kChunks = D / 16;   // 8-pair chunks per head half
     constexpr int kTokens = kWriteThreads / 64;   // one wave per token
 
     __shared__ double s_cos[kTokens][kHalf];
@@ -125,109 +211,96 @@ __global__ __launch_bounds__(kWriteThreads) void rope_write_kernel(WriteArgs a, 
     }
     __syncthreads();
     if (!pos_ok) return;                             // uniform per wave; no barrier follows
-    const long long page = slot >> 6;
-    const int in_page = (int)(slot & (kPage - 1));
 
-    // ---- q and k heads: norm, rotate, round, store ------------------------
     const int n_rope_heads = a.n_q_heads + a.n_kv_heads;
-    const int n_items = n_rope_heads * kLanesPerHead;
-    const int n_iter = (n_items + 63) / 64;
+    const int n_iter = (n_rope_heads * kLanesPerHead + 63) / 64;
     for (int it = 0; it < n_iter; ++it) {         // uniform trip count: shuffles stay wave-wide
-        const int item = it * 64 + lane;
-        const int head = item / kLanesPerHead;
-        const int j = item % kLanesPerHead;
-        const bool active = head < n_rope_heads && j < kChunks;
-        const bool is_q = head < a.n_q_heads;
-
-        double xl[8], xh[8];
-        const uint16_t* src = nullptr;
-        if (active) {
-            src = is_q ? a.q + (long long)t * a.ld_in + (long long)head * D
-                       : a.k + (long long)t * a.ld_in + (long long)(head - a.n_q_heads) * D;
-            const u32x4 lo = *reinterpret_cast<const u32x4*>(src + 8 * j);
-            const u32x4 hi = *reinterpret_cast<const u32x4*>(src + kHalf + 8 * j);
-#pragma unroll
-            for (int w = 0; w < 4; ++w) {
-                xl[2 * w] = (double)bf16_to_f32(lo[w] & 0xffffu);
-                xl[2 * w + 1] = (double)bf16_to_f32(lo[w] >> 16);
-                xh[2 * w] = (double)bf16_to_f32(hi[w] & 0xffffu);
-                xh[2 * w + 1] = (double)bf16_to_f32(hi[w] >> 16);
-            }
-        } else {
-#pragma unroll
-            for (int i = 0; i < 8; ++i) { xl[i] = 0.0; xh[i] = 0.0; }
-        }
-
-        if (a.qk_norm) {
-            double ss = 0.0;
-#pragma unroll
-            for (int i = 0; i < 8; ++i) ss += xl[i] * xl[i] + xh[i] * xh[i];
-            ss += __shfl_xor(ss, 1);
-            ss += __shfl_xor(ss, 2);
-            ss += __shfl_xor(ss, 4);
-            if (active) {
-                const double denom = sqrt(ss / (double)D + a.eps);
-                const uint16_t* g = is_q ? a.q_gain : a.k_gain;
-                const u32x4 gl = *reinterpret_cast<const u32x4*>(g + 8 * j);
-                const u32x4 gh = *reinterpret_cast<const u32x4*>(g + kHalf + 8 * j);
-#pragma unroll
-                for (int w = 0; w < 4; ++w) {
-                    xl[2 * w] = (double)bf16_to_f32(gl[w] & 0xffffu) * xl[2 * w] / denom;
-                    xl[2 * w + 1] = (double)bf16_to_f32(gl[w] >> 16) * xl[2 * w + 1] / denom;
-                    xh[2 * w] = (double)bf16_to_f32(gh[w] & 0xffffu) * xh[2 * w] / denom;
-                    xh[2 * w + 1] = (double)bf16_to_f32(gh[w] >> 16) * xh[2 * w + 1] / denom;
-                }
-            }
-        }
-        if (!active) continue;
-
-        u32x4 ol, oh;
-#pragma unroll
-        for (int w = 0; w < 4; ++w) {
-            uint32_t l2[2], h2[2];
-#pragma unroll
-            for (int e = 0; e < 2; ++e) {
-                const int i = 2 * w + e;
-                const double c = s_cos[wave][8 * j + i];
-                const double s = s_sin[wave][8 * j + i];
-                l2[e] = f64_to_bf16(xl[i] * c - xh[i] * s);
-                h2[e] = f64_to_bf16(xh[i] * c + xl[i] * s);
-            }
-            ol[w] = l2[0] | (l2[1] << 16);
-            oh[w] = h2[0] | (h2[1] << 16);
-        }
-        uint16_t* dst;
-        if (is_q) {
-            dst = a.q_out + (long long)t * a.ld_q_out + (long long)head * D;
-        } else {
-            if (slot < 0) continue;
-            const int kh = head - a.n_q_heads;
-            uint16_t* tile = a.k_pool + (page * a.n_kv_heads + kh) * (long long)(D * kPage);
-            *reinterpret_cast<u32x4*>(tile + k_tile_offset(in_page, 8 * j, D)) = ol;
-            *reinterpret_cast<u32x4*>(tile + k_tile_offset(in_page, kHalf + 8 * j, D)) = oh;
-            continue;
-        }
-        *reinterpret_cast<u32x4*>(dst + 8 * j) = ol;
-        *reinterpret_cast<u32x4*>(dst + kHalf + 8 * j) = oh;
+        u32x4 lo, hi;
+        int head, j;
+        bool active;
+        load_item<D>(a, t, it * 64 + lane, n_rope_heads, lo, hi, head, j, active);
+        rope_item<D>(a, t, head, j, active, lo, hi, s_cos[wave], s_sin[wave], slot);
     }
-
     // V is written by the tile workgroups
+}
+
+// Few tokens: one workgroup (4 waves) per token, so a token's heads run in
+// parallel; the first two items of every thread are loaded before the
+// sin/cos, so the row loads overlap them.
+template <int D>
+__global__ __launch_bounds__(kWriteThreads) void rope_write_token_kernel(WriteArgs a, int n_vtiles) {
+    if ((int)blockIdx.x < n_vtiles * a.n_kv_heads) {  // uniform per workgroup
+        write_v_tile<D>(a, (blockIdx.x / a.n_kv_heads) * kVTile, blockIdx.x % a.n_kv_heads);
+        return;
+    }
+    constexpr int kHalf = D / 2;
+    constexpr int kBatch = 2;
+    __shared__ double s_cos[kHalf];
+    __shared__ double s_sin[kHalf];
+    __shared__ long long s_slot;
+
+    const int tid = threadIdx.x;
+    const int t = (int)blockIdx.x - n_vtiles * a.n_kv_heads;
+    const int p = a.positions[t];
+    if (p < 0 || p >= a.max_position) {                       // uniform per workgroup
+        if (tid == 0) atomicOr(a.err, kErrPosition);
+        return;
+    }
+    const int n_rope_heads = a.n_q_heads + a.n_kv_heads;
+    const int n_iter = (n_rope_heads * kLanesPerHead + kWriteThreads - 1) / kWriteThreads;
+    long long slot = -1;
+    for (int it0 = 0; it0 < n_iter; it0 += kBatch) {
+        u32x4 lo[kBatch], hi[kBatch];
+        int head[kBatch], j[kBatch];
+        bool active[kBatch];
+#pragma unroll
+        for (int b = 0; b < kBatch; ++b)
+            load_item<D>(a, t, (it0 + b) * kWriteThreads + tid, n_rope_heads, lo[b], hi[b], head[b], j[b],
+                         active[b]);
+        if (it0 == 0) {                                       // uniform: the angle table, once
+            if (tid == 0) s_slot = token_slot(a, t, p, true);
+            for (int i = tid; i < kHalf; i += kWriteThreads) {
+                const double ang = (double)p * a.inv_freq[i];
+                double sn, cs;
+                sincos(ang, &sn, &cs);
+                s_sin[i] = sn;
+                s_cos[i] = cs;
+            }
+            __syncthreads();
+            slot = s_slot;
+        }
+#pragma unroll
+        for (int b = 0; b < kBatch; ++b)
+            if (it0 + b < n_iter)                            // uniform
+                rope_item<D>(a, t, head[b], j[b], active[b], lo[b], hi[b], s_cos, s_sin, slot);
+    }
 }
 
 }  // namespace
 
+// Below kWideTokens tokens the one-workgroup-per-token form fills the chip
+// better; above it, one wave per token.
+constexpr int kWideTokens = 4096;
+
 hipError_t launch_write(const WriteArgs& a, hipStream_t s, Profiler* prof) {
     if (a.n_tokens <= 0) return hipSuccess;
     const int n_vtiles = (a.n_tokens + kVTile - 1) / kVTile;
-    const int n_token_groups = (a.n_tokens + kWriteThreads / 64 - 1) / (kWriteThreads / 64);
-    dim3 grid(n_vtiles * a.n_kv_heads + n_token_groups), block(kWriteThreads);
+    const bool per_token = a.n_tokens < kWideTokens;
+    const int n_token_blocks = per_token ? a.n_tokens : (a.n_tokens + kWriteThreads / 64 - 1) / (kWriteThreads / 64);
+    dim3 grid(n_vtiles * a.n_kv_heads + n_token_blocks), block(kWriteThreads);
     if (prof) prof->begin(DAP_KERNEL_WRITE, s);
+#define DAP_WRITE_CASE(DD)                                                                                       \
+    case DD:                                                                                                    \
+        if (per_token) hipLaunchKernelGGL(rope_write_token_kernel<DD>, grid, block, 0, s, a, n_vtiles);         \
+        else hipLaunchKernelGGL(rope_write_kernel<DD>, grid, block, 0, s, a, n_vtiles);                         \
+        break;
     switch (a.head_dim) {
-        case 64: hipLaunchKernelGGL(rope_write_kernel<64>, grid, block, 0, s, a, n_vtiles); break;
-        case 96: hipLaunchKernelGGL(rope_write_kernel<96>, grid, block, 0, s, a, n_vtiles); break;
-        case 128: hipLaunchKernelGGL(rope_write_kernel<128>, grid, block, 0, s, a, n_vtiles); break;
+        DAP_WRITE_CASE(64)
+        DAP_WRITE_CASE(96)
+        DAP_WRITE_CASE(128)
         default: return hipErrorInvalidValue;
     }
+#undef DAP_WRITE_CASE
     if (prof) prof->end(DAP_KERNEL_WRITE, s);
     return hipGetLastError();
 }
