@@ -298,7 +298,7 @@ int do_prefill(dap_handle* h, const uint16_t* q, int64_t ld_q, int32_t n_tokens,
     const size_t need = dap::prefill_workspace(n_tokens, n_segments, h->group);
     DAP_REQUIRE(workspace && workspace_bytes >= need && aligned16(workspace), DAP_WORKSPACE_TOO_SMALL,
                 "workspace must be 16-byte aligned and at least dap_prefill_workspace_bytes()");
-    const long long blocks = (long long)((need / sizeof(int)) - 2) * h->m.n_kv_heads;
+    const long long blocks = (long long)dap::tile_cap(n_tokens, n_segments, h->group) * h->m.n_kv_heads;
     DAP_REQUIRE(blocks < (1ll << 31), DAP_UNSUPPORTED, "too many prefill tiles for one launch");
     if (h->validate) {
         std::vector<int32_t> hp, hs, ht;

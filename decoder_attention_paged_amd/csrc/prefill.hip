@@ -29,6 +29,7 @@ namespace {
 constexpr int kPrefillWaves = 8;
 constexpr int kPrefillThreads = 64 * kPrefillWaves;
 constexpr int kTilesThreads = 1024;
+constexpr int kSortTiles = 4096;       // tiles ordered longest first by the tile pass
 constexpr float kLog2e = 1.4426950408889634f;
 constexpr unsigned kErrSegments = 32u;
 
@@ -36,12 +37,17 @@ __device__ __forceinline__ bf16x8 as_bf16x8(u32x4 u) { return __builtin_bit_cast
 
 // ---------------------------------------------------------------- tile list
 // tiles[k] = first token of tile k (k < n_tiles), tiles[n_tiles] = end of the
-// last tile, tiles[cap + 1] = n_tiles (at most cap tiles are kept).
+// last tile, tiles[cap + 1] = n_tiles (at most cap tiles are kept), then
+// tiles[cap + 2 + i] = the tile the i-th workgroup group takes.
 // A tile starts where (t - start of t's run) is a multiple of bm.
-__global__ __launch_bounds__(kTilesThreads) void prefill_tiles_kernel(const int32_t* __restrict__ seg, int n,
-                                                                      int bm, int cap, int* __restrict__ tiles,
-                                                                      unsigned* err) {
+__global__ __launch_bounds__(kTilesThreads) void prefill_tiles_kernel(const int32_t* __restrict__ seg,
+                                                                      const int32_t* __restrict__ pos, int n,
+                                                                      int bm, int cap, int window,
+                                                                      int* __restrict__ tiles, unsigned* err) {
     __shared__ int s_scan[kTilesThreads];
+    __shared__ int s_start[kSortTiles + 1];
+    __shared__ int s_work[kSortTiles];
+    __shared__ int s_idx[kSortTiles];
     const int tid = threadIdx.x;
     const int chunk = (n + kTilesThreads - 1) / kTilesThreads;
     const int c0 = min(n, tid * chunk);
@@ -87,6 +93,7 @@ __global__ __launch_bounds__(kTilesThreads) void prefill_tiles_kernel(const int3
         if ((t - r) % bm == 0) {
             // index cap holds the first dropped tile's start (the end of the last kept one)
             if (idx <= cap) tiles[idx] = t;
+            if (idx < kSortTiles) s_start[idx] = t;
             ++idx;
         }
     }
@@ -95,6 +102,54 @@ __global__ __launch_bounds__(kTilesThreads) void prefill_tiles_kernel(const int3
         else atomicOr(err, kErrSegments);
         tiles[cap + 1] = min(total, cap);
     }
+
+    // Dispatch order, longest first: tile k's work is the pages its tokens
+    // attend (first token's window start to last token's position). A
+    // bitonic sort in LDS orders the tiles by it, so the workgroups with the
+    // most pages start first and the short ones fill in behind them.
+    const int n_tiles = min(total, cap);
+    int* order = tiles + cap + 2;
+    if (n_tiles > kSortTiles) {                       // too many to sort here: pack order
+        for (int k = tid; k < n_tiles; k += kTilesThreads) order[k] = k;
+        return;
+    }
+    if (tid == 0) s_start[n_tiles] = n;
+    __syncthreads();
+    int m2 = 1;
+    while (m2 < n_tiles) m2 <<= 1;
+    for (int k = tid; k < m2; k += kTilesThreads) {
+        int w = -1;
+        if (k < n_tiles) {
+            const int t0 = s_start[k];
+            const int t1 = min(s_start[k + 1], t0 + bm);
+            const int pf = pos[t0], pl = pos[t1 - 1];
+            const int lo = window > 0 ? max(0, pf - window + 1) : 0;
+            w = max(0, (pl >> 6) - (max(lo, 0) >> 6) + 1);
+        }
+        s_work[k] = w;
+        s_idx[k] = k;
+    }
+    __syncthreads();
+    for (int size = 2; size <= m2; size <<= 1) {
+        for (int stride = size >> 1; stride > 0; stride >>= 1) {
+            for (int k = tid; k < m2; k += kTilesThreads) {
+                const int l = k ^ stride;
+                if (l > k) {
+                    const bool desc = (k & size) == 0;   // the whole sequence ends descending
+                    const int wk = s_work[k], wl = s_work[l];
+                    if (desc ? (wk < wl) : (wk > wl)) {
+                        s_work[k] = wl;
+                        s_work[l] = wk;
+                        const int ik = s_idx[k];
+                        s_idx[k] = s_idx[l];
+                        s_idx[l] = ik;
+                    }
+                }
+            }
+            __syncthreads();
+        }
+    }
+    for (int k = tid; k < n_tiles; k += kTilesThreads) order[k] = s_idx[k];
 }
 
 __device__ __forceinline__ int wave_min(int v) {
@@ -130,8 +185,9 @@ __global__ __launch_bounds__(kPrefillThreads) void prefill_kernel(AttnArgs a, co
 
     const int n_tiles = tiles[cap + 1];
     const int kh = blockIdx.x % a.n_kv_heads;
-    const int tile = blockIdx.x / a.n_kv_heads;
-    if (tile >= n_tiles) return;
+    const int slot = blockIdx.x / a.n_kv_heads;
+    if (slot >= n_tiles) return;
+    const int tile = tiles[cap + 2 + slot];          // longest tiles first
     const int t0 = tiles[tile];
     const int t1 = min(tiles[tile + 1], t0 + BM);
 
@@ -386,15 +442,15 @@ hipError_t launch_prefill_d(const AttnArgs& a, int G, int cap, const int* tiles,
     }
 }
 
+}  // namespace
+
 int tile_cap(int n_tokens, int n_segments, int group) {
     const int bm = 32 * kPrefillWaves / group;
     return (n_tokens + bm - 1) / bm + n_segments;
 }
 
-}  // namespace
-
 size_t prefill_workspace(int n_tokens, int n_segments, int group) {
-    return (size_t)(tile_cap(n_tokens, n_segments, group) + 2) * sizeof(int);
+    return (size_t)(2 * tile_cap(n_tokens, n_segments, group) + 2) * sizeof(int);   // starts, count, order
 }
 
 hipError_t launch_prefill(const AttnArgs& a, int n_segments, void* workspace, hipStream_t s, Profiler* prof) {
@@ -403,8 +459,8 @@ hipError_t launch_prefill(const AttnArgs& a, int n_segments, void* workspace, hi
     const int cap = tile_cap(a.n_tokens, n_segments, G);
     int* tiles = static_cast<int*>(workspace);
     if (prof) prof->begin(DAP_KERNEL_PREFILL_TILES, s);
-    hipLaunchKernelGGL(prefill_tiles_kernel, dim3(1), dim3(kTilesThreads), 0, s, a.rows, a.n_tokens,
-                       32 * kPrefillWaves / G, cap, tiles, a.err);
+    hipLaunchKernelGGL(prefill_tiles_kernel, dim3(1), dim3(kTilesThreads), 0, s, a.rows, a.positions, a.n_tokens,
+                       32 * kPrefillWaves / G, cap, a.window, tiles, a.err);
     if (prof) prof->end(DAP_KERNEL_PREFILL_TILES, s);
     hipError_t e = hipGetLastError();
     if (e != hipSuccess) return e;
