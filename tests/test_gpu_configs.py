@@ -202,3 +202,55 @@ def test_qwen3_step_paged():
     torch.cuda.synchronize()
     assert torch.equal(o_pre.view(torch.int16), out[:P].view(torch.int16))
     assert torch.equal(o_dec.view(torch.int16), out[P:].view(torch.int16))
+
+
+def test_mistral_contiguous_decode_rows():
+    """The Mistral rows through dap_decode_rows on a contiguous cache (the
+    identity table), at full size: written token bits and sampled rows."""
+    wl = W.mistral_contiguous()
+    m = wl.model
+    h = handle_for(m)
+    kp, vp = device_pools(wl)
+    R = wl.n_dec
+    max_seq = wl.table.shape[1] * 64
+    qkv = wl.qkv("step", R, "cuda")
+    out = h.decode_rows(*_split(qkv, m), torch_i32(wl.dec_positions), kp, vp, max_seq=max_seq)
+    torch.cuda.synchronize()
+    _, q_bits, k_bits, v_bits = oracle_front(wl, to_np_bits(qkv), wl.dec_positions)
+    slots = pages.slot_of(wl.table, wl.dec_rows, wl.dec_positions)
+    _check_written(wl, kp, vp, slots, k_bits, v_bits, "contiguous new token")
+    op = OraclePool(wl, "cuda")
+    op.write(slots, k_bits, v_bits)
+    order = np.argsort(wl.dec_positions)
+    pick = np.unique(np.concatenate([order[:3], order[-3:], np.random.default_rng(2).choice(R, 6, replace=False)]))
+    ref = oracle_attention(wl, op, bf16.to_f64(q_bits[pick]), wl.dec_positions[pick], wl.dec_rows[pick])
+    check_close(to_np_bits(out)[pick], ref, "contiguous decode (sampled rows)")
+
+
+def test_packed_training_forward():
+    """8 Llama-3.1-shaped prompts of 4096 tokens through dap_packed at full
+    size: sampled query tokens of every prompt (first, last and a spread)
+    against the oracle's in-pass attention over the prompt's own keys."""
+    wl = W.packed_train()
+    m = wl.model
+    h = handle_for(m)
+    T = wl.n_pre
+    qkv = wl.qkv("train", T, "cuda")
+    pos, seg = wl.pre_positions, wl.pre_segments
+    out = h.packed(*_split(qkv, m), torch_i32(pos), torch_i32(seg), n_segments=8)
+    torch.cuda.synchronize()
+    _, q_bits, k_bits, v_bits = oracle_front(wl, to_np_bits(qkv), pos)
+    qf, kf, vf = bf16.to_f64(q_bits), bf16.to_f64(k_bits), bf16.to_f64(v_bits)
+    got = to_np_bits(out)
+    rng = np.random.default_rng(3)
+    picks, refs = [], []
+    for sgi in range(8):
+        idx = np.nonzero(seg == sgi)[0]
+        idx = idx[np.argsort(pos[idx])]
+        K, V = np.swapaxes(kf[idx], 0, 1), np.swapaxes(vf[idx], 0, 1)
+        sample = np.unique(np.concatenate([[0, 1, 63, 64, len(idx) - 1], rng.choice(len(idx), 6, replace=False)]))
+        for k in sample:
+            t = idx[k]
+            picks.append(t)
+            refs.append(attention.attend_one(qf[t], K, V, int(pos[t]), m.window))
+    check_close(got[np.array(picks)], np.stack(refs), "packed training forward (sampled tokens)")
