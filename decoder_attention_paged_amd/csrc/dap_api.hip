@@ -765,36 +765,48 @@ int dap_step_paged(dap_handle* h, const uint16_t* q, const uint16_t* k, const ui
     DAP_REQUIRE(workspace && workspace_bytes >= need && aligned16(workspace), DAP_WORKSPACE_TOO_SMALL,
                 "workspace must be 16-byte aligned and at least dap_step_workspace_bytes()");
     hipStream_t s = static_cast<hipStream_t>(stream);
-    const int n_all = n_prompt + n_step;
-    int rc = do_write(h, q, k, v, ld_in, n_all, positions, rows, slots, table, table_ld, n_table_rows, q_gain, k_gain,
-                      q_out, ld_q_out, k_pool, v_pool, n_pages, s);
-    if (rc) return rc;
     const size_t dec_bytes = align256(dap_decode_workspace_bytes(h, n_step));
+    char* pre_ws = static_cast<char*>(workspace) + dec_bytes;
+    const size_t pre_bytes = workspace_bytes - dec_bytes;
+    const uint16_t* q_step = q_out + (int64_t)n_prompt * ld_q_out;
+    uint16_t* out_step = out + (int64_t)n_prompt * ld_out;
     // With both parts present (and outside validate mode, which synchronises
-    // per call), the prefill runs on the handle's second stream: its MFMA
-    // work overlaps the decode's HBM streaming. Fork after the write, join
-    // before returning, so the caller's stream orders everything as before.
-    const bool overlap = n_prompt > 0 && n_step > 0 && !h->validate;
-    hipStream_t ps = s;
-    if (overlap) {
+    // per call), the prompt part (its write, then the prefill) runs on the
+    // handle's second stream while the step part (its write, then the decode)
+    // runs on `stream`: the prefill's matrix work overlaps the decode's HBM
+    // streaming, and the decode waits only for its own rows' writes. Fork
+    // first, join before returning (also after an error), so the caller's
+    // stream orders everything as before.
+    if (n_prompt > 0 && n_step > 0 && !h->validate) {
         hipError_t e = hipEventRecord(h->fork_ev, s);
         if (e == hipSuccess) e = hipStreamWaitEvent(h->side, h->fork_ev, 0);
         if (e != hipSuccess) return hip_fail(e, "forking the prefill stream");
-        ps = h->side;
-    }
-    if (n_prompt > 0)
-        rc = do_prefill(h, q_out, ld_q_out, n_prompt, positions, rows, n_segments, table, table_ld, n_table_rows,
-                        k_pool, v_pool, n_pages, out, ld_out, static_cast<char*>(workspace) + dec_bytes,
-                        workspace_bytes - dec_bytes, ps);
-    if (n_step > 0 && rc == DAP_OK)
-        rc = do_decode(h, q_out + (int64_t)n_prompt * ld_q_out, ld_q_out, n_step, positions + n_prompt,
-                       rows + n_prompt, table, table_ld, n_table_rows, k_pool, v_pool, n_pages,
-                       out + (int64_t)n_prompt * ld_out, ld_out, workspace, dec_bytes, s);
-    if (overlap) {                                   // join even after an error: nothing outlives the call
-        hipError_t e = hipEventRecord(h->join_ev, h->side);
+        int rc = do_write(h, q + (int64_t)n_prompt * ld_in, k + (int64_t)n_prompt * ld_in,
+                          v + (int64_t)n_prompt * ld_in, ld_in, n_step, positions + n_prompt, rows + n_prompt,
+                          slots ? slots + n_prompt : nullptr, table, table_ld, n_table_rows, q_gain, k_gain,
+                          q_out + (int64_t)n_prompt * ld_q_out, ld_q_out, k_pool, v_pool, n_pages, s);
+        if (rc == DAP_OK)
+            rc = do_write(h, q, k, v, ld_in, n_prompt, positions, rows, slots, table, table_ld, n_table_rows, q_gain,
+                          k_gain, q_out, ld_q_out, k_pool, v_pool, n_pages, h->side);
+        if (rc == DAP_OK)
+            rc = do_prefill(h, q_out, ld_q_out, n_prompt, positions, rows, n_segments, table, table_ld, n_table_rows,
+                            k_pool, v_pool, n_pages, out, ld_out, pre_ws, pre_bytes, h->side);
+        if (rc == DAP_OK)
+            rc = do_decode(h, q_step, ld_q_out, n_step, positions + n_prompt, rows + n_prompt, table, table_ld,
+                           n_table_rows, k_pool, v_pool, n_pages, out_step, ld_out, workspace, dec_bytes, s);
+        e = hipEventRecord(h->join_ev, h->side);
         if (e == hipSuccess) e = hipStreamWaitEvent(s, h->join_ev, 0);
         if (e != hipSuccess && rc == DAP_OK) return hip_fail(e, "joining the prefill stream");
+        return rc;
     }
+    int rc = do_write(h, q, k, v, ld_in, n_prompt + n_step, positions, rows, slots, table, table_ld, n_table_rows,
+                      q_gain, k_gain, q_out, ld_q_out, k_pool, v_pool, n_pages, s);
+    if (n_prompt > 0 && rc == DAP_OK)
+        rc = do_prefill(h, q_out, ld_q_out, n_prompt, positions, rows, n_segments, table, table_ld, n_table_rows,
+                        k_pool, v_pool, n_pages, out, ld_out, pre_ws, pre_bytes, s);
+    if (n_step > 0 && rc == DAP_OK)
+        rc = do_decode(h, q_step, ld_q_out, n_step, positions + n_prompt, rows + n_prompt, table, table_ld,
+                       n_table_rows, k_pool, v_pool, n_pages, out_step, ld_out, workspace, dec_bytes, s);
     return rc;
 }
 

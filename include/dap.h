@@ -194,11 +194,16 @@ int dap_attn_decode_paged(dap_handle* handle,
  * Tokens 0..n_prompt-1 are prompt tokens, tokens n_prompt..n_prompt+n_step-1
  * the decode tokens. rows[t] is every token's table row (for prompt tokens
  * also its segment); positions, rows, slots (nullable) cover all tokens.
- * Runs the write over all tokens, then the packed prefill on the prompt
- * tokens and the decode on the step tokens, reading q from q_out. With both
- * parts present the prefill runs on a second stream the handle owns (forked
- * from and joined back to `stream` with events), so its matrix work overlaps
- * the decode's memory streaming; the call still orders everything on
+ * Computes what writing every token first, then the packed prefill on the
+ * prompt tokens and the decode on the step tokens (q read from q_out)
+ * computes. With both parts present (validate mode off) the prompt part, its
+ * write then its prefill, runs on a second stream the handle owns (forked
+ * from and joined back to `stream` with events) while the step part, its
+ * write then its decode, runs on `stream`: the prefill's matrix work overlaps
+ * the decode's memory streaming. The two orders agree when no token's visible
+ * keys include a slot that a token of the other part writes in the same call,
+ * which holds whenever a page being written belongs to one row (rows may
+ * still share read-only prefix pages). The call still orders everything on
  * `stream`. Calls on one handle must not be issued from several host threads
  * at once (the fork and join events are the handle's).
  * out : [n_prompt + n_step][ld_out] bf16.
