@@ -435,6 +435,25 @@ def copy_ceiling(nbytes: int = 1 << 30, reps: int = 10) -> float:
     return round(gbps, 1)
 
 
+def cold_steps(b: "Bench", n: int, flush_bytes: int = 512 << 20) -> np.ndarray:
+    """Step times (ms) with the 256 MB last-level cache flushed before each
+    step: a 512 MB buffer is read and rewritten between steps, outside the
+    events around the step, so no K/V page is cache-resident when it starts."""
+    buf = torch.zeros(flush_bytes, dtype=torch.uint8, device="cuda")
+    out = []
+    for _ in range(n):
+        buf.add_(1)
+        a, c = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        a.record()
+        b.step()
+        c.record()
+        torch.cuda.synchronize()
+        out.append(a.elapsed_time(c))
+    del buf
+    torch.cuda.empty_cache()
+    return np.array(out)
+
+
 # --------------------------------------------------------------------------- traffic counters
 def traffic_for(kernel: str, workload: str):
     """HBM bytes per launch from the committed rocprofv3 counter summary,
@@ -503,6 +522,8 @@ def main():
     kern_ms = {k: (v[0] / v[1] if v[1] else 0.0) for k, v in prof.items()}
     step_ms = np.array([marks[i].elapsed_time(marks[i + 1]) for i in range(args.steps)])
 
+    cold_ms = cold_steps(b, min(args.steps, 10))
+
     m = b.m
     value = b.bytes / (ms_per_step * 1e-3) / 1e9
     dom = max(("decode", "prefill", "write"), key=lambda k: prof[k][0])
@@ -542,6 +563,8 @@ def main():
         "kernel_avg_ms": {k: round(v, 5) for k, v in kern_ms.items() if prof[k][1]},
         "step_ms_median": round(float(np.median(step_ms)), 4),
         "step_ms_spread": [round(float(step_ms.min()), 4), round(float(step_ms.max()), 4)],
+        "cold_step_ms_median": round(float(np.median(cold_ms)), 4),
+        "cold_gbps": round(b.bytes / (float(np.median(cold_ms)) * 1e-3) / 1e9, 2),
         "hbm_copy_ceiling_gbps": copy_ceiling(),
     }
     if b.flops and b.name == "qwen3":

@@ -34,6 +34,8 @@ constexpr float kLog2e = 1.4426950408889634f;
 constexpr unsigned kErrSegments = 32u;
 
 __device__ __forceinline__ bf16x8 as_bf16x8(u32x4 u) { return __builtin_bit_cast(bf16x8, u); }
+typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
+constexpr bf16x2 kOnes2 = {(__bf16)1.0f, (__bf16)1.0f};
 
 // ---------------------------------------------------------------- tile list
 // tiles[k] = first token of tile k (k < n_tiles), tiles[n_tiles] = end of the
@@ -265,9 +267,23 @@ __global__ __launch_bounds__(kPrefillThreads) void prefill_kernel(AttnArgs a, co
     const int j_first = kmin >> 6;
     const int j_last = kmax >> 6;
 
+    // The row's page ids, 64 at a time in one register (lane l holds the id
+    // of page j_base + l), so the loop reads them with readlane instead of
+    // waiting on a table load after every barrier. Pages are asked for in
+    // increasing order; a new window is loaded every 64 pages.
+    int j_base = j_first;
+    int ids = j_base + lane <= j_last ? tr[j_base + lane] : -1;
+    auto page_id = [&](int j) -> int {
+        if (j - j_base >= 64) {                        // uniform
+            j_base += 64;
+            ids = j_base + lane <= j_last ? tr[j_base + lane] : -1;
+        }
+        return __builtin_amdgcn_readlane(ids, j - j_base);
+    };
+
     u32x4 pk[kChunks], pv[kChunks];
     auto prefetch = [&](int j) -> bool {
-        const int pg = tr[j];
+        const int pg = page_id(j);
         if (pg < 0 || pg >= a.n_pages) return false;
         const uint16_t* kt = a.k_pool + ((long long)pg * a.n_kv_heads + kh) * (kPage * D);
         const uint16_t* vt = a.v_pool + ((long long)pg * a.n_kv_heads + kh) * (kPage * D);
@@ -373,18 +389,16 @@ __global__ __launch_bounds__(kPrefillThreads) void prefill_kernel(AttnArgs a, co
             m = m_new;
         }
         const float m_ref = m == -INFINITY ? 0.f : m;     // a row with nothing visible yet
-        float ps = 0.f;
 #pragma unroll
         for (int blk = 0; blk < 2; ++blk)
 #pragma unroll
-            for (int r = 0; r < 16; ++r) {
-                const float e = __builtin_amdgcn_exp2f(__builtin_fmaf(sc[blk][r], c, -m_ref));
-                sc[blk][r] = e;
-                ps += e;
-            }
-        lsum += ps;
+            for (int r = 0; r < 16; ++r)
+                sc[blk][r] = __builtin_amdgcn_exp2f(__builtin_fmaf(sc[blk][r], c, -m_ref));
 
-        // O^T += V^T P^T : four 16-key steps
+        // O^T += V^T P^T : four 16-key steps. The row sum adds the bf16
+        // weights the MFMAs use, two per dot2 (the normaliser is then the sum
+        // of exactly the weights applied to V).
+        float ps0 = 0.f, ps1 = 0.f;
 #pragma unroll
         for (int t = 0; t < 4; ++t) {
             bf16x8 pf;
@@ -393,7 +407,12 @@ __global__ __launch_bounds__(kPrefillThreads) void prefill_kernel(AttnArgs a, co
 #pragma unroll
             for (int db = 0; db < kDimBlocks; ++db)
                 o[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(as_bf16x8(vfr[t][db]), pf, o[db], 0, 0, 0);
+            ps0 = __builtin_amdgcn_fdot2_f32_bf16(__builtin_shufflevector(pf, pf, 0, 1), kOnes2, ps0, false);
+            ps1 = __builtin_amdgcn_fdot2_f32_bf16(__builtin_shufflevector(pf, pf, 2, 3), kOnes2, ps1, false);
+            ps0 = __builtin_amdgcn_fdot2_f32_bf16(__builtin_shufflevector(pf, pf, 4, 5), kOnes2, ps0, false);
+            ps1 = __builtin_amdgcn_fdot2_f32_bf16(__builtin_shufflevector(pf, pf, 6, 7), kOnes2, ps1, false);
         }
+        lsum += ps0 + ps1;
         }
         // next page into the other buffer (its previous contents were last read
         // before the previous barrier), then one barrier
