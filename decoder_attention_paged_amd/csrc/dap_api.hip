@@ -295,10 +295,10 @@ int do_prefill(dap_handle* h, const uint16_t* q, int64_t ld_q, int32_t n_tokens,
         return rc;
     DAP_REQUIRE(segments && aligned4(segments), DAP_INVALID_ARG, "segments must be a non-null aligned pointer");
     DAP_REQUIRE(n_segments > 0, DAP_INVALID_ARG, "n_segments must be positive");
-    const size_t need = dap::prefill_workspace(n_tokens, n_segments, h->group);
+    const size_t need = dap::prefill_workspace(n_tokens, n_segments, h->group, h->m.head_dim);
     DAP_REQUIRE(workspace && workspace_bytes >= need && aligned16(workspace), DAP_WORKSPACE_TOO_SMALL,
                 "workspace must be 16-byte aligned and at least dap_prefill_workspace_bytes()");
-    const long long blocks = (long long)dap::tile_cap(n_tokens, n_segments, h->group) * h->m.n_kv_heads;
+    const long long blocks = (long long)dap::tile_cap(n_tokens, n_segments, h->group, h->m.head_dim) * h->m.n_kv_heads;
     DAP_REQUIRE(blocks < (1ll << 31), DAP_UNSUPPORTED, "too many prefill tiles for one launch");
     if (h->validate) {
         std::vector<int32_t> hp, hs, ht;
@@ -365,7 +365,7 @@ struct Carve {
 };
 
 size_t attn_workspace(const dap_handle* h, long long n_tokens, int n_groups) {
-    size_t b = dap::prefill_workspace((int)n_tokens, n_groups, h->group);
+    size_t b = dap::prefill_workspace((int)n_tokens, n_groups, h->group, h->m.head_dim);
     if (n_tokens <= dap::kMaxDecodeRows) {
         const dap::DecodePlan plan = dap::decode_plan((int)n_tokens, h->m.n_q_heads, h->m.n_kv_heads, h->m.head_dim,
                                                       h->m.window, h->m.max_position);
@@ -490,7 +490,7 @@ InpassLayout inpass_layout(const dap_handle* h, void* ws, long long n_tokens, in
     L.rel = c.take<int32_t>(n_tokens);
     L.q_rope = c.take<uint16_t>((size_t)n_tokens * h->m.n_q_heads * h->m.head_dim);
     L.prefill = c.base ? c.base + c.off : nullptr;
-    c.off += align256(dap::prefill_workspace((int)n_tokens, n_segments, h->group));
+    c.off += align256(dap::prefill_workspace((int)n_tokens, n_segments, h->group, h->m.head_dim));
     const size_t tile = (size_t)h->m.n_kv_heads * dap::kPage * h->m.head_dim;
     L.k_pool = c.take<uint16_t>((size_t)L.capacity * tile);
     L.v_pool = c.take<uint16_t>((size_t)L.capacity * tile);
@@ -719,7 +719,7 @@ int dap_rope_qknorm_write_pages(dap_handle* h, const uint16_t* q, const uint16_t
 
 size_t dap_prefill_workspace_bytes(const dap_handle* h, int32_t n_tokens, int32_t n_segments) {
     if (!h || n_tokens < 0 || n_segments < 0) return 0;
-    return dap::prefill_workspace(n_tokens, std::max(n_segments, 1), h->group);
+    return dap::prefill_workspace(n_tokens, std::max(n_segments, 1), h->group, h->m.head_dim);
 }
 
 int dap_attn_prefill_packed(dap_handle* h, const uint16_t* q, int64_t ld_q, int32_t n_tokens, const int32_t* positions,

@@ -184,8 +184,8 @@ hipError_t launch_decode(const AttnArgs& a, const DecodePlan& plan, void* worksp
                          Profiler* prof);
 
 // Prefill: tile list sizing and launch.
-size_t prefill_workspace(int n_tokens, int n_segments, int group);
-int tile_cap(int n_tokens, int n_segments, int group);   // most tiles one prefill call may form
+size_t prefill_workspace(int n_tokens, int n_segments, int group, int head_dim);
+int tile_cap(int n_tokens, int n_segments, int group, int head_dim);   // most tiles one prefill call may form
 hipError_t launch_prefill(const AttnArgs& a, int n_segments, void* workspace, hipStream_t s, Profiler* prof);
 
 // Index preparation for the contiguous-cache entries: per-token positions and

@@ -8,10 +8,14 @@
 // position, which covers chunks and shared prefixes).
 //
 // A tile-list pass cuts the packed tokens into runs of equal segment id and
-// each run into tiles of at most 256/g tokens. One workgroup (8 waves) takes
+// each run into tiles of at most 32*W/g tokens. One workgroup (W waves) takes
 // one (tile, kv head): wave w owns 32 query rows = one of the g query heads
 // sharing the kv head, for 32 of the tile's tokens, so each K/V page tile is
-// read from memory once per workgroup for all g heads and 256 query rows.
+// read from memory once per workgroup for all g heads and 32*W query rows.
+// W is 8 at head_dim 128 (one workgroup per CU, most rows per staged page)
+// and 4 below, where the softmax outweighs the matrix work per key: two
+// workgroups share a CU and, not tied by one barrier, overlap each other's
+// MFMA and VALU phases, and shorter tiles waste less at the causal diagonal.
 // Per 64-key page the workgroup stages K (key-major) and V^T (dim-major)
 // into one of two LDS buffers (one barrier per page), and each
 // wave computes S^T = K Q^T and O^T += V^T P^T with 32x32x16 bf16 MFMAs and
@@ -26,11 +30,12 @@ namespace dap {
 
 namespace {
 
-constexpr int kPrefillWaves = 8;
-constexpr int kPrefillThreads = 64 * kPrefillWaves;
+// waves per prefill workgroup at head_dim D
+__host__ __device__ constexpr int prefill_waves(int D) { return D >= 128 ? 8 : 4; }
 constexpr int kTilesThreads = 1024;
 constexpr int kSortTiles = 4096;       // tiles ordered longest first by the tile pass
 constexpr float kLog2e = 1.4426950408889634f;
+constexpr float kLazyMax = 8.f;        // log2 of the largest softmax weight before a rescale
 constexpr unsigned kErrSegments = 32u;
 
 __device__ __forceinline__ bf16x8 as_bf16x8(u32x4 u) { return __builtin_bit_cast(bf16x8, u); }
@@ -171,9 +176,10 @@ __device__ __forceinline__ int wave_max(int v) {
 __device__ __forceinline__ int swap23(int i) { return (i & ~12) | ((i & 4) << 1) | ((i & 8) >> 1); }
 
 template <int D, int G>
-__global__ __launch_bounds__(kPrefillThreads) void prefill_kernel(AttnArgs a, const int* __restrict__ tiles,
-                                                                  int cap) {
-    constexpr int BM = 32 * kPrefillWaves / G;   // tokens per tile
+__global__ __launch_bounds__(64 * prefill_waves(D), 8 / prefill_waves(D))
+void prefill_kernel(AttnArgs a, const int* __restrict__ tiles, int cap) {
+    constexpr int kPrefillThreads = 64 * prefill_waves(D);
+    constexpr int BM = 32 * prefill_waves(D) / G;   // tokens per tile
     constexpr int KS = D + 8;           // LDS row stride of K (elements)
     constexpr int VS = kPage + 8;       // LDS row stride of V^T (elements)
     constexpr int kSteps = D / 16;      // QK k-steps
@@ -378,15 +384,18 @@ __global__ __launch_bounds__(kPrefillThreads) void prefill_kernel(AttnArgs a, co
 #pragma unroll
             for (int r = 0; r < 16; ++r) mx = fmaxf(mx, sc[blk][r]);
         mx = fmaxf(mx, __shfl_xor(mx, 32));
-        // running max in scaled log2 units; O and l are rescaled only when
-        // some row's max moved (rare once a row has seen a few pages)
-        const float m_new = fmaxf(m, mx * c);
-        if (__any(m_new > m)) {
-            const float alpha = m_new > m ? __builtin_amdgcn_exp2f(m - m_new) : 1.f;
+        // Reference max in scaled log2 units: it moves to a row's new max only
+        // when a score exceeds it by more than 2^kLazyMax (any visible key
+        // sets an unset one), so the weights stay at most 2^kLazyMax and O and
+        // l are rescaled on a row's first pages only.
+        const float ms = mx * c;
+        const bool move = ms > m + kLazyMax;
+        if (__any(move)) {
+            const float alpha = move ? __builtin_amdgcn_exp2f(m - ms) : 1.f;
             lsum *= alpha;
 #pragma unroll
             for (int db = 0; db < kDimBlocks; ++db) o[db] *= alpha;
-            m = m_new;
+            if (move) m = ms;
         }
         const float m_ref = m == -INFINITY ? 0.f : m;     // a row with nothing visible yet
 #pragma unroll
@@ -446,8 +455,8 @@ hipError_t launch_prefill_dg(const AttnArgs& a, int cap, const int* tiles, hipSt
         if (e != hipSuccess) return e;
         configured = true;
     }
-    hipLaunchKernelGGL((prefill_kernel<D, G>), dim3((unsigned)cap * a.n_kv_heads), dim3(kPrefillThreads), lds, s, a,
-                       tiles, cap);
+    hipLaunchKernelGGL((prefill_kernel<D, G>), dim3((unsigned)cap * a.n_kv_heads), dim3(64 * prefill_waves(D)), lds,
+                       s, a, tiles, cap);
     return hipGetLastError();
 }
 
@@ -463,23 +472,23 @@ hipError_t launch_prefill_d(const AttnArgs& a, int G, int cap, const int* tiles,
 
 }  // namespace
 
-int tile_cap(int n_tokens, int n_segments, int group) {
-    const int bm = 32 * kPrefillWaves / group;
+int tile_cap(int n_tokens, int n_segments, int group, int head_dim) {
+    const int bm = 32 * prefill_waves(head_dim) / group;
     return (n_tokens + bm - 1) / bm + n_segments;
 }
 
-size_t prefill_workspace(int n_tokens, int n_segments, int group) {
-    return (size_t)(2 * tile_cap(n_tokens, n_segments, group) + 2) * sizeof(int);   // starts, count, order
+size_t prefill_workspace(int n_tokens, int n_segments, int group, int head_dim) {
+    return (size_t)(2 * tile_cap(n_tokens, n_segments, group, head_dim) + 2) * sizeof(int);   // starts, count, order
 }
 
 hipError_t launch_prefill(const AttnArgs& a, int n_segments, void* workspace, hipStream_t s, Profiler* prof) {
     if (a.n_tokens <= 0) return hipSuccess;
     const int G = a.n_q_heads / a.n_kv_heads;
-    const int cap = tile_cap(a.n_tokens, n_segments, G);
+    const int cap = tile_cap(a.n_tokens, n_segments, G, a.head_dim);
     int* tiles = static_cast<int*>(workspace);
     if (prof) prof->begin(DAP_KERNEL_PREFILL_TILES, s);
     hipLaunchKernelGGL(prefill_tiles_kernel, dim3(1), dim3(kTilesThreads), 0, s, a.rows, a.positions, a.n_tokens,
-                       32 * kPrefillWaves / G, cap, a.window, tiles, a.err);
+                       32 * prefill_waves(a.head_dim) / G, cap, a.window, tiles, a.err);
     if (prof) prof->end(DAP_KERNEL_PREFILL_TILES, s);
     hipError_t e = hipGetLastError();
     if (e != hipSuccess) return e;
