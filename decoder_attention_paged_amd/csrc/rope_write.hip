@@ -61,34 +61,57 @@ __device__ __forceinline__ long long token_slot(const WriteArgs& a, int t, int p
 }
 
 // V of kVTile consecutive tokens, per kv head: rows read coalesced, turned
-// around in LDS, and stored with lanes running along tokens, so the tokens
-// of one page land as contiguous runs of 8 keys per dim.
+// around in LDS, and stored along tokens. The tile layout keeps 8 consecutive
+// keys of a dim in one 16-byte chunk, so 8 tokens of the tile whose slots are
+// one aligned run of 8 (the usual case: a prompt's tokens fill their pages in
+// order) are stored as one chunk; any other group is stored element by element.
 template <int D>
 __device__ __forceinline__ void write_v_tile(const WriteArgs& a, int t0, int kh) {
-    constexpr int VS = kVTile + 2;     // LDS row stride (elements), odd word stride
-    __shared__ uint16_t s_v[D * VS];
+    // LDS: dim d's 64 tokens in 8 groups of 8, group g stored at position
+    // g ^ ((d >> 3) & 7): the transpose writes (16 lanes, one token, 16 dims)
+    // spread over 8 banks and every group stays one aligned 16-byte chunk
+    __shared__ __attribute__((aligned(16))) uint16_t s_v[D * kVTile];
     __shared__ long long s_slot[kVTile];
+    __shared__ int s_run[kVTile / 8];  // group g's 8 slots form one aligned run
+    auto at = [](int d, int tt) { return d * kVTile + 8 * ((tt >> 3) ^ ((d >> 3) & 7)) + (tt & 7); };
     const int tid = threadIdx.x;
     const int n = min(kVTile, a.n_tokens - t0);
     if (tid < kVTile) s_slot[tid] = tid < n ? token_slot(a, t0 + tid, a.positions[t0 + tid], false) : -1;
-    {
-        for (int c = tid; c < n * (D / 8); c += kWriteThreads) {
-            const int tt = c / (D / 8), d8 = c % (D / 8);
-            const u32x4 x = *reinterpret_cast<const u32x4*>(a.v + (long long)(t0 + tt) * a.ld_in +
-                                                            (long long)kh * D + 8 * d8);
+    for (int c = tid; c < n * (D / 8); c += kWriteThreads) {
+        const int tt = c / (D / 8), d8 = c % (D / 8);
+        const u32x4 x = *reinterpret_cast<const u32x4*>(a.v + (long long)(t0 + tt) * a.ld_in +
+                                                        (long long)kh * D + 8 * d8);
 #pragma unroll
-            for (int w = 0; w < 4; ++w) {
-                s_v[(8 * d8 + 2 * w) * VS + tt] = (uint16_t)(x[w] & 0xffffu);
-                s_v[(8 * d8 + 2 * w + 1) * VS + tt] = (uint16_t)(x[w] >> 16);
-            }
+        for (int w = 0; w < 4; ++w) {
+            s_v[at(8 * d8 + 2 * w, tt)] = (uint16_t)(x[w] & 0xffffu);
+            s_v[at(8 * d8 + 2 * w + 1, tt)] = (uint16_t)(x[w] >> 16);
         }
-        __syncthreads();
-        for (int e = tid; e < D * kVTile; e += kWriteThreads) {
-            const int d = e / kVTile, tt = e % kVTile;
+    }
+    __syncthreads();
+    if (tid < kVTile / 8) {
+        const long long s0 = s_slot[8 * tid];
+        bool run = s0 >= 0 && (s0 & 7) == 0;
+#pragma unroll
+        for (int i = 1; i < 8; ++i) run = run && s_slot[8 * tid + i] == s0 + i;
+        s_run[tid] = run;
+    }
+    __syncthreads();
+    // one item per (dim, group of 8 tokens)
+    for (int e = tid; e < D * (kVTile / 8); e += kWriteThreads) {
+        const int d = e / (kVTile / 8), g = e % (kVTile / 8);
+        if (s_run[g]) {
+            const long long slot = s_slot[8 * g];
+            const u32x4 x = *reinterpret_cast<const u32x4*>(&s_v[at(d, 8 * g)]);
+            *reinterpret_cast<u32x4*>(a.v_pool + ((slot >> 6) * a.n_kv_heads + kh) * (long long)(D * kPage) +
+                                      v_tile_offset((int)(slot & (kPage - 1)), d, D)) = x;
+            continue;
+        }
+        for (int i = 0; i < 8; ++i) {
+            const int tt = 8 * g + i;
             const long long slot = s_slot[tt];
             if (tt >= n || slot < 0) continue;
             a.v_pool[((slot >> 6) * a.n_kv_heads + kh) * (long long)(D * kPage) +
-                     v_tile_offset((int)(slot & (kPage - 1)), d, D)] = s_v[d * VS + tt];
+                     v_tile_offset((int)(slot & (kPage - 1)), d, D)] = s_v[at(d, tt)];
         }
     }
 }
