@@ -3,10 +3,10 @@
 // One wave per token for q and k: the token's D/2 rotation angles p*f[i]
 // and their sine/cosine are computed once in float64 into LDS, then every q
 // and k head of the token is normed (optionally), rotated and rounded to
-// bf16 once. In the same launch, one workgroup per (64 tokens, kv head)
-// copies v into the V tiles through an LDS transpose, so the consecutive
-// slots of one dim are written as contiguous runs (the tile layout keeps 8
-// consecutive keys of a dim together). Page tiles are in the library's
+// bf16 once. In the same launch, after the token workgroups, one workgroup
+// per (64 tokens, kv head) copies v into the V tiles through an LDS
+// transpose, so the consecutive slots of one dim are written as contiguous
+// runs (the tile layout keeps 8 consecutive keys of a dim together). Page tiles are in the library's
 // tile layout, 16-byte chunks in the order the decode loads them. This is a
 // bandwidth-bound pass (a few flops per byte), so the
 // float64 arithmetic costs nothing and lets K pages match the float64
@@ -202,26 +202,42 @@ __device__ __forceinline__ void load_item(const WriteArgs& a, int t, int item, i
     }
 }
 
-// Many tokens: one wave per token, four tokens per workgroup.
+// Many tokens: one wave per token, four tokens per workgroup. Items (8
+// lanes per head) are software-pipelined two deep: the rows of item i+1 are
+// loaded before item i is rotated and stored (q_out may alias q, so the
+// compiler would not move a later load above an earlier store by itself),
+// and the first item's rows are loaded before the sin/cos.
 template <int D>
-__global__ __launch_bounds__(kWriteThreads) void rope_write_kernel(WriteArgs a, int n_vtiles) {
-    if ((int)blockIdx.x < n_vtiles * a.n_kv_heads) {  // uniform per workgroup
-        write_v_tile<D>(a, (blockIdx.x / a.n_kv_heads) * kVTile, blockIdx.x % a.n_kv_heads);
-        return;
-    }
+__global__ __launch_bounds__(kWriteThreads) void rope_write_kernel(WriteArgs a) {
     static_assert(D % 16 == 0 && D / 16 <= kLanesPerHead, "head_dim");
     constexpr int kHalf = D / 2;
     constexpr int kTokens = kWriteThreads / 64;   // one wave per token
+    // the token workgroups come first, so their latency-bound chains start
+    // before the V workgroups fill the machine
+    const int n_tb = (a.n_tokens + kTokens - 1) / kTokens;
+    if ((int)blockIdx.x >= n_tb) {                   // uniform per workgroup
+        const int vb = (int)blockIdx.x - n_tb;
+        write_v_tile<D>(a, (vb / a.n_kv_heads) * kVTile, vb % a.n_kv_heads);
+        return;
+    }
 
     __shared__ double s_cos[kTokens][kHalf];
     __shared__ double s_sin[kTokens][kHalf];
 
     const int wave = threadIdx.x >> 6;
     const int lane = threadIdx.x & 63;
-    const int t = ((int)blockIdx.x - n_vtiles * a.n_kv_heads) * kTokens + wave;
+    const int t = (int)blockIdx.x * kTokens + wave;
     const bool have = t < a.n_tokens;                // uniform per wave
     const int p = have ? a.positions[t] : 0;
     const bool pos_ok = have && p >= 0 && p < a.max_position;
+    const int n_rope_heads = a.n_q_heads + a.n_kv_heads;
+    const int n_iter = (n_rope_heads * kLanesPerHead + 63) / 64;
+
+    u32x4 lo0, hi0, lo1, hi1;
+    int head0, j0, head1, j1;
+    bool act0, act1;
+    if (pos_ok) load_item<D>(a, t, lane, n_rope_heads, lo0, hi0, head0, j0, act0);
+
     long long slot = -1;
     if (have && lane == 0) slot = token_slot(a, t, p, true);
     slot = __shfl(slot, 0);
@@ -235,14 +251,12 @@ __global__ __launch_bounds__(kWriteThreads) void rope_write_kernel(WriteArgs a, 
     __syncthreads();
     if (!pos_ok) return;                             // uniform per wave; no barrier follows
 
-    const int n_rope_heads = a.n_q_heads + a.n_kv_heads;
-    const int n_iter = (n_rope_heads * kLanesPerHead + 63) / 64;
-    for (int it = 0; it < n_iter; ++it) {         // uniform trip count: shuffles stay wave-wide
-        u32x4 lo, hi;
-        int head, j;
-        bool active;
-        load_item<D>(a, t, it * 64 + lane, n_rope_heads, lo, hi, head, j, active);
-        rope_item<D>(a, t, head, j, active, lo, hi, s_cos[wave], s_sin[wave], slot);
+    for (int it = 0; it < n_iter; it += 2) {         // uniform trip count: shuffles stay wave-wide
+        const bool two = it + 1 < n_iter;
+        if (two) load_item<D>(a, t, (it + 1) * 64 + lane, n_rope_heads, lo1, hi1, head1, j1, act1);
+        rope_item<D>(a, t, head0, j0, act0, lo0, hi0, s_cos[wave], s_sin[wave], slot);
+        if (it + 2 < n_iter) load_item<D>(a, t, (it + 2) * 64 + lane, n_rope_heads, lo0, hi0, head0, j0, act0);
+        if (two) rope_item<D>(a, t, head1, j1, act1, lo1, hi1, s_cos[wave], s_sin[wave], slot);
     }
     // V is written by the tile workgroups
 }
@@ -251,9 +265,10 @@ __global__ __launch_bounds__(kWriteThreads) void rope_write_kernel(WriteArgs a, 
 // parallel; the first two items of every thread are loaded before the
 // sin/cos, so the row loads overlap them.
 template <int D>
-__global__ __launch_bounds__(kWriteThreads) void rope_write_token_kernel(WriteArgs a, int n_vtiles) {
-    if ((int)blockIdx.x < n_vtiles * a.n_kv_heads) {  // uniform per workgroup
-        write_v_tile<D>(a, (blockIdx.x / a.n_kv_heads) * kVTile, blockIdx.x % a.n_kv_heads);
+__global__ __launch_bounds__(kWriteThreads) void rope_write_token_kernel(WriteArgs a) {
+    if ((int)blockIdx.x >= a.n_tokens) {             // uniform per workgroup: V after the tokens
+        const int vb = (int)blockIdx.x - a.n_tokens;
+        write_v_tile<D>(a, (vb / a.n_kv_heads) * kVTile, vb % a.n_kv_heads);
         return;
     }
     constexpr int kHalf = D / 2;
@@ -263,7 +278,7 @@ __global__ __launch_bounds__(kWriteThreads) void rope_write_token_kernel(WriteAr
     __shared__ long long s_slot;
 
     const int tid = threadIdx.x;
-    const int t = (int)blockIdx.x - n_vtiles * a.n_kv_heads;
+    const int t = (int)blockIdx.x;
     const int p = a.positions[t];
     if (p < 0 || p >= a.max_position) {                       // uniform per workgroup
         if (tid == 0) atomicOr(a.err, kErrPosition);
@@ -314,8 +329,8 @@ hipError_t launch_write(const WriteArgs& a, hipStream_t s, Profiler* prof) {
     if (prof) prof->begin(DAP_KERNEL_WRITE, s);
 #define DAP_WRITE_CASE(DD)                                                                                       \
     case DD:                                                                                                    \
-        if (per_token) hipLaunchKernelGGL(rope_write_token_kernel<DD>, grid, block, 0, s, a, n_vtiles);         \
-        else hipLaunchKernelGGL(rope_write_kernel<DD>, grid, block, 0, s, a, n_vtiles);                         \
+        if (per_token) hipLaunchKernelGGL(rope_write_token_kernel<DD>, grid, block, 0, s, a);                   \
+        else hipLaunchKernelGGL(rope_write_kernel<DD>, grid, block, 0, s, a);                                   \
         break;
     switch (a.head_dim) {
         DAP_WRITE_CASE(64)
