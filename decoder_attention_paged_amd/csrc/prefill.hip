@@ -46,12 +46,55 @@ constexpr bf16x2 kOnes2 = {(__bf16)1.0f, (__bf16)1.0f};
 // tiles[k] = first token of tile k (k < n_tiles), tiles[n_tiles] = end of the
 // last tile, tiles[cap + 1] = n_tiles (at most cap tiles are kept), then
 // tiles[cap + 2 + i] = the tile the i-th workgroup group takes.
-// A tile starts where (t - start of t's run) is a multiple of bm.
+// A tile starts where (t - start of t's run) is a multiple of bm (a power of
+// two). Thread i owns a contiguous chunk of the tokens; each chunk is read
+// once, eight loads in flight, and its run starts kept in a bit mask (chunks
+// above 64 tokens, past 65536 tokens in a call, read the segments again).
+
+// exclusive max-scan (identity -1) and inclusive sum-scan over the block:
+// within each wave by shuffles, then one exchange of the wave totals
+__device__ __forceinline__ int block_excl_max(int v, int* s_w) {
+    const int lane = threadIdx.x & 63, wv = threadIdx.x >> 6;
+    int x = v;
+#pragma unroll
+    for (int o = 1; o < 64; o <<= 1) {
+        const int y = __shfl_up(x, o);
+        if (lane >= o) x = max(x, y);
+    }
+    if (lane == 63) s_w[wv] = x;
+    __syncthreads();
+    int pre = -1;
+    for (int w = 0; w < wv; ++w) pre = max(pre, s_w[w]);
+    int ex = __shfl_up(x, 1);
+    if (lane == 0) ex = -1;
+    __syncthreads();
+    return max(ex, pre);
+}
+__device__ __forceinline__ int block_incl_sum(int v, int* s_w, int& total) {
+    const int lane = threadIdx.x & 63, wv = threadIdx.x >> 6;
+    int x = v;
+#pragma unroll
+    for (int o = 1; o < 64; o <<= 1) {
+        const int y = __shfl_up(x, o);
+        if (lane >= o) x += y;
+    }
+    if (lane == 63) s_w[wv] = x;
+    __syncthreads();
+    int pre = 0;
+    total = 0;
+    for (int w = 0; w < (int)(blockDim.x >> 6); ++w) {
+        if (w < wv) pre += s_w[w];
+        total += s_w[w];
+    }
+    __syncthreads();
+    return x + pre;
+}
+
 __global__ __launch_bounds__(kTilesThreads) void prefill_tiles_kernel(const int32_t* __restrict__ seg,
                                                                       const int32_t* __restrict__ pos, int n,
                                                                       int bm, int cap, int window,
                                                                       int* __restrict__ tiles, unsigned* err) {
-    __shared__ int s_scan[kTilesThreads];
+    __shared__ int s_w[kTilesThreads / 64];
     __shared__ int s_start[kSortTiles + 1];
     __shared__ int s_work[kSortTiles];
     __shared__ int s_idx[kSortTiles];
@@ -59,45 +102,44 @@ __global__ __launch_bounds__(kTilesThreads) void prefill_tiles_kernel(const int3
     const int chunk = (n + kTilesThreads - 1) / kTilesThreads;
     const int c0 = min(n, tid * chunk);
     const int c1 = min(n, c0 + chunk);
+    const bool masked = chunk <= 64;
+    auto starts_run = [&](int t) { return t == 0 || seg[t] != seg[t - 1]; };
 
-    // last run start inside my chunk (-1 if none)
+    // run starts of my chunk; the last one
+    unsigned long long flags = 0ull;
     int my_start = -1;
-    for (int t = c0; t < c1; ++t)
-        if (t == 0 || seg[t] != seg[t - 1]) my_start = t;
-    // exclusive max-scan of run starts
-    s_scan[tid] = my_start;
-    __syncthreads();
-    for (int off = 1; off < kTilesThreads; off <<= 1) {
-        const int v = tid >= off ? s_scan[tid - off] : -1;
-        __syncthreads();
-        s_scan[tid] = max(s_scan[tid], v);
-        __syncthreads();
+    for (int b = c0; b < c1; b += 8) {
+        int v[9];
+#pragma unroll
+        for (int i = 0; i < 9; ++i) {
+            const int t = b - 1 + i;
+            v[i] = t >= 0 && t < c1 ? seg[t] : 0;
+        }
+#pragma unroll
+        for (int i = 1; i < 9; ++i) {
+            const int t = b - 1 + i;
+            if (t < c1 && (t == 0 || v[i] != v[i - 1])) {
+                my_start = t;
+                if (masked) flags |= 1ull << (t - c0);
+            }
+        }
     }
-    int rs = tid > 0 ? s_scan[tid - 1] : -1;
-    __syncthreads();
+    auto is_start = [&](int t) { return masked ? ((flags >> (t - c0)) & 1ull) != 0 : starts_run(t); };
+    const int rs = block_excl_max(my_start, s_w);   // the run my chunk starts in
 
-    // count tile starts in my chunk
+    // tile starts in my chunk, their count and place
     int cnt = 0;
     int r = rs;
     for (int t = c0; t < c1; ++t) {
-        if (t == 0 || seg[t] != seg[t - 1]) r = t;
-        if ((t - r) % bm == 0) ++cnt;
+        if (is_start(t)) r = t;
+        if (((t - r) & (bm - 1)) == 0) ++cnt;
     }
-    // inclusive sum-scan of counts
-    s_scan[tid] = cnt;
-    __syncthreads();
-    for (int off = 1; off < kTilesThreads; off <<= 1) {
-        const int v = tid >= off ? s_scan[tid - off] : 0;
-        __syncthreads();
-        s_scan[tid] += v;
-        __syncthreads();
-    }
-    int idx = s_scan[tid] - cnt;
-    const int total = s_scan[kTilesThreads - 1];
+    int total;
+    int idx = block_incl_sum(cnt, s_w, total) - cnt;
     r = rs;
     for (int t = c0; t < c1; ++t) {
-        if (t == 0 || seg[t] != seg[t - 1]) r = t;
-        if ((t - r) % bm == 0) {
+        if (is_start(t)) r = t;
+        if (((t - r) & (bm - 1)) == 0) {
             // index cap holds the first dropped tile's start (the end of the last kept one)
             if (idx <= cap) tiles[idx] = t;
             if (idx < kSortTiles) s_start[idx] = t;
@@ -112,8 +154,9 @@ __global__ __launch_bounds__(kTilesThreads) void prefill_tiles_kernel(const int3
 
     // Dispatch order, longest first: tile k's work is the pages its tokens
     // attend (first token's window start to last token's position). A
-    // bitonic sort in LDS orders the tiles by it, so the workgroups with the
-    // most pages start first and the short ones fill in behind them.
+    // bitonic sort orders the tiles by it (in one wave's registers up to 64
+    // tiles, in LDS up to kSortTiles), so the workgroups with the most pages
+    // start first and the short ones fill in behind them.
     const int n_tiles = min(total, cap);
     int* order = tiles + cap + 2;
     if (n_tiles > kSortTiles) {                       // too many to sort here: pack order
@@ -122,18 +165,38 @@ __global__ __launch_bounds__(kTilesThreads) void prefill_tiles_kernel(const int3
     }
     if (tid == 0) s_start[n_tiles] = n;
     __syncthreads();
+    auto work = [&](int k) {
+        const int t0 = s_start[k];
+        const int t1 = min(s_start[k + 1], t0 + bm);
+        const int pf = pos[t0], pl = pos[t1 - 1];
+        const int lo = window > 0 ? max(0, pf - window + 1) : 0;
+        return max(0, (pl >> 6) - (lo >> 6) + 1);
+    };
+    if (n_tiles <= 64) {
+        if (tid >= 64) return;
+        int w = tid < n_tiles ? work(tid) : -1;       // padding sorts last
+        int id = tid;
+        for (int size = 2; size <= 64; size <<= 1) {
+            for (int stride = size >> 1; stride > 0; stride >>= 1) {
+                const int ow = __shfl_xor(w, stride);
+                const int oid = __shfl_xor(id, stride);
+                const bool lower = (tid & stride) == 0;
+                const bool desc = (tid & size) == 0;   // the whole sequence ends descending
+                // the lower lane of a pair keeps the larger work in a descending block
+                const bool take = lower == desc ? ow > w : ow < w;
+                if (take) {
+                    w = ow;
+                    id = oid;
+                }
+            }
+        }
+        if (tid < n_tiles) order[tid] = id;
+        return;
+    }
     int m2 = 1;
     while (m2 < n_tiles) m2 <<= 1;
     for (int k = tid; k < m2; k += kTilesThreads) {
-        int w = -1;
-        if (k < n_tiles) {
-            const int t0 = s_start[k];
-            const int t1 = min(s_start[k + 1], t0 + bm);
-            const int pf = pos[t0], pl = pos[t1 - 1];
-            const int lo = window > 0 ? max(0, pf - window + 1) : 0;
-            w = max(0, (pl >> 6) - (max(lo, 0) >> 6) + 1);
-        }
-        s_work[k] = w;
+        s_work[k] = k < n_tiles ? work(k) : -1;
         s_idx[k] = k;
     }
     __syncthreads();

@@ -181,6 +181,42 @@ def test_write_matches_oracle_bits(model, explicit_slots):
     assert torch.equal(vb.view(torch.int16), va.view(torch.int16))
 
 
+@pytest.mark.parametrize("d,n_tokens", [(64, 161), (96, 161), (128, 161), (128, 4100)])
+def test_write_runs_of_slots(d, n_tokens):
+    """Prompt-shaped writes: a run from an 8-aligned position with a partial
+    last group of 8, then a run from a misaligned position, in the same V
+    tiles (groups of 8 slots that form one aligned run are stored whole, the
+    others element by element); both write forms (per token below 4096
+    tokens, per wave from 4096 up). Pools must match the oracle bit for bit
+    and nothing else may change."""
+    model = _model(16, 4, d, 0, max_position=8192, theta=1e4)
+    wl = _workload(model, 2, 128, f"wr-runs-{d}-{n_tokens}")
+    kp, vp = device_pools(wl)
+    k_before, v_before = kp.clone(), vp.clone()
+    n0 = n_tokens - 61
+    rows = np.concatenate([np.zeros(n0), np.ones(61)]).astype(np.int32)
+    positions = np.concatenate([np.arange(64, 64 + n0), np.arange(37, 98)]).astype(np.int32)
+    qkv = W.normal_matrix(wl.key("qkv"), n_tokens, model.qkv_width, "cuda")
+    D, hq, hkv = model.head_dim, model.n_q_heads, model.n_kv_heads
+    h = handle_for(model)
+    q_out = h.rope_qknorm_write_pages(qkv[:, :hq * D], qkv[:, hq * D:(hq + hkv) * D], qkv[:, (hq + hkv) * D:],
+                                      torch_i32(positions), kp, vp, rows=torch_i32(rows), table=torch_i32(wl.table))
+    torch.cuda.synchronize()
+    _, q_bits, k_bits, v_bits = oracle_front(wl, to_np_bits(qkv), positions, None)
+    check_bits(to_np_bits(q_out).reshape(n_tokens, hq, D), q_bits, "q_out")
+    slots = pages.slot_of(wl.table, rows, positions)
+    kg, vg = dap.gather_slots(kp, vp, slots)
+    check_bits(to_np_bits(kg), k_bits, "K pages")
+    assert np.array_equal(to_np_bits(vg), v_bits), "V pages must be a bit copy"
+    s = torch.as_tensor(slots, device="cuda")
+    kb, vb = dap.pool_logical(k_before, v_before)
+    ka, va = dap.pool_logical(kp, vp)
+    kb[s // 64, :, s % 64, :] = ka[s // 64, :, s % 64, :]
+    vb[s // 64, :, s % 64, :] = va[s // 64, :, s % 64, :]
+    assert torch.equal(kb.view(torch.int16), ka.view(torch.int16))
+    assert torch.equal(vb.view(torch.int16), va.view(torch.int16))
+
+
 def test_write_in_place_q():
     model = _model(32, 8, 128, 0, 512, theta=1e6, eps=1e-6)
     wl = _workload(model, 2, 8, "wr-inplace")
