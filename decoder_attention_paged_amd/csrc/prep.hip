@@ -68,14 +68,48 @@ __global__ __launch_bounds__(kInpassThreads) void inpass_prep_kernel(InpassPrep 
         s_hi[s] = -1;
     }
     __syncthreads();
-    for (int t = tid; t < p.n_tokens; t += kInpassThreads) {
-        const int sg = p.segments[t], pos = p.positions[t];
-        if (sg < 0 || sg >= ns) {
-            atomicOr(p.err, kErrRow);
-            continue;
+    // A wave whose tokens all lie in one segment (the usual case: segments
+    // are runs of the pack) reduces their positions by shuffles and makes
+    // one update; otherwise each lane updates its own segment. Four rounds'
+    // tokens are loaded before any is used, to keep loads in flight.
+    constexpr int kRounds = 4;
+    const int lane = tid & 63;
+    for (int tb = tid - lane; tb < p.n_tokens; tb += kRounds * kInpassThreads) {
+        int sgs[kRounds], poss[kRounds];
+#pragma unroll
+        for (int k = 0; k < kRounds; ++k) {
+            const int t = tb + k * kInpassThreads + lane;
+            sgs[k] = t < p.n_tokens ? p.segments[t] : -1;
+            poss[k] = t < p.n_tokens ? p.positions[t] : 0;
         }
-        atomicMin(&s_lo[sg], pos);
-        atomicMax(&s_hi[sg], pos);
+#pragma unroll
+        for (int k = 0; k < kRounds; ++k) {
+            const int t = tb + k * kInpassThreads + lane;
+            const bool valid = t < p.n_tokens;
+            const int sg = sgs[k], pos = poss[k];
+            if (tb + k * kInpassThreads >= p.n_tokens) break;     // uniform: no token left in this round
+            const int s0 = __builtin_amdgcn_readfirstlane(sg);  // lane 0 holds a token
+            if (__ballot(valid && sg != s0) == 0 && s0 >= 0 && s0 < ns) {   // uniform
+                int lo = valid ? pos : 0x7fffffff, hi = valid ? pos : -1;
+#pragma unroll
+                for (int o = 32; o > 0; o >>= 1) {
+                    lo = min(lo, __shfl_xor(lo, o));
+                    hi = max(hi, __shfl_xor(hi, o));
+                }
+                if (lane == 0) {
+                    atomicMin(&s_lo[s0], lo);
+                    atomicMax(&s_hi[s0], hi);
+                }
+                continue;
+            }
+            if (!valid) continue;
+            if (sg < 0 || sg >= ns) {
+                atomicOr(p.err, kErrRow);
+                continue;
+            }
+            atomicMin(&s_lo[sg], pos);
+            atomicMax(&s_hi[sg], pos);
+        }
     }
     __syncthreads();
     // pages per segment, exclusive scan (each thread owns a run of segments)
@@ -112,20 +146,32 @@ __global__ __launch_bounds__(kInpassThreads) void inpass_prep_kernel(InpassPrep 
         const int pg = s_first[s] + j;
         p.table[i] = (j < pages && pg < p.capacity) ? pg : -1;
     }
-    for (int t = tid; t < p.n_tokens; t += kInpassThreads) {
-        const int sg = p.segments[t];
-        if (sg < 0 || sg >= ns) {
-            p.slots[t] = -1;
-            p.rel_positions[t] = 0;
-            continue;
+    for (int tb = tid; tb < p.n_tokens; tb += kRounds * kInpassThreads) {
+        int sgs[kRounds], poss[kRounds];
+#pragma unroll
+        for (int k = 0; k < kRounds; ++k) {
+            const int t = tb + k * kInpassThreads;
+            sgs[k] = t < p.n_tokens ? p.segments[t] : -1;
+            poss[k] = t < p.n_tokens ? p.positions[t] : 0;
         }
-        const int rel = p.positions[t] - s_lo[sg];
-        const int j = rel / kPage;
-        const int pg = s_first[sg] + j;
-        const bool fits = j < p.table_ld && pg < p.capacity;
-        if (!fits) atomicOr(p.err, kErrSpan);
-        p.slots[t] = fits ? pg * kPage + rel % kPage : -1;
-        p.rel_positions[t] = rel;
+#pragma unroll
+        for (int k = 0; k < kRounds; ++k) {
+            const int t = tb + k * kInpassThreads;
+            if (t >= p.n_tokens) break;
+            const int sg = sgs[k];
+            if (sg < 0 || sg >= ns) {
+                p.slots[t] = -1;
+                p.rel_positions[t] = 0;
+                continue;
+            }
+            const int rel = poss[k] - s_lo[sg];
+            const int j = rel / kPage;
+            const int pg = s_first[sg] + j;
+            const bool fits = j < p.table_ld && pg < p.capacity;
+            if (!fits) atomicOr(p.err, kErrSpan);
+            p.slots[t] = fits ? pg * kPage + rel % kPage : -1;
+            p.rel_positions[t] = rel;
+        }
     }
 }
 
