@@ -78,37 +78,23 @@ __device__ __forceinline__ uint32_t f32_to_bf16(float x) {
     return u >> 16;
 }
 
-// float64 -> bf16 in one rounding, to nearest even, from the bit pattern.
-// Normal bf16 range keeps 7 stored mantissa bits of the 52; below 2^-126 the
-// grid is the subnormal quantum 2^-133; a carry out of the largest finite
-// value gives infinity.
-__device__ __forceinline__ uint32_t f64_to_bf16(double x) {
-    const uint64_t b = (uint64_t)__double_as_longlong(x);
-    const uint32_t sign = (uint32_t)(b >> 48) & 0x8000u;
-    const uint64_t a = b & 0x7fffffffffffffffull;
-    if (a > 0x7ff0000000000000ull) return sign | 0x7fc0u;           // NaN
-    const int e = (int)(a >> 52) - 1023;                             // unbiased exponent
-    if (e > 127) return sign | 0x7f80u;                              // inf or too large
-    const uint64_t mant = a & 0x000fffffffffffffull;
-    if (e >= -126) {
-        const uint32_t kept = (uint32_t)(mant >> 45);
-        const uint64_t rem = mant & ((1ull << 45) - 1);
-        const uint64_t half = 1ull << 44;
-        uint32_t r = ((uint32_t)(e + 127) << 7) | kept;
-        if (rem > half || (rem == half && (kept & 1u))) r += 1;     // may carry into exponent
-        return sign | r;
-    }
-    if ((a >> 52) == 0) return sign;                                 // fp64 zero/subnormal
-    // bf16 subnormal: value = full * 2^(e-52); quantum 2^-133
-    const uint64_t full = mant | (1ull << 52);
-    const int shift = 45 + (-126 - e);                               // >= 46
-    if (shift >= 64) return sign;
-    const uint64_t kept = full >> shift;
-    const uint64_t rem = full & ((1ull << shift) - 1);
-    const uint64_t half = 1ull << (shift - 1);
-    uint64_t r = kept;
-    if (rem > half || (rem == half && (kept & 1u))) r += 1;
-    return sign | (uint32_t)r;
+// float64 -> bf16, rounded to nearest even as if in one step, without
+// branches: first to float32 rounding to odd (to nearest, then, when that was
+// inexact and left the last bit even, one step toward x), then to bf16 to
+// nearest even. Rounding to odd with at least two spare bits followed by
+// rounding to nearest gives the directly rounded result (the double-rounding
+// theorem of Boldo and Melquiond); float32 keeps 16 bits more than bf16 at
+// every exponent, subnormals included, and the two share the exponent range.
+// NaN gives the quiet NaN 0x7fc0 with x's sign.
+__host__ __device__ __forceinline__ uint32_t f64_to_bf16(double x) {
+    const float f = (float)x;
+    const double back = (double)f;
+    uint32_t u = __builtin_bit_cast(uint32_t, f);
+    const bool step = back != x && !(u & 1u) && (u & 0x7f800000u) != 0x7f800000u;
+    u += step ? (fabs(back) > fabs(x) ? 0xffffffffu : 1u) : 0u;
+    const uint32_t r = (u + 0x7fffu + ((u >> 16) & 1u)) >> 16;
+    const uint32_t nan = ((uint32_t)(__builtin_bit_cast(uint64_t, x) >> 48) & 0x8000u) | 0x7fc0u;
+    return x != x ? nan : r;
 }
 
 // ---------------------------------------------------------------------------
