@@ -76,9 +76,6 @@ struct dap_handle {
     int validate;
     dap::ProfilerState* prof_state;
     dap::Profiler prof;
-    // step_paged runs its prefill on this second stream, beside the decode
-    hipStream_t side;
-    hipEvent_t fork_ev, join_ev;
     dap::Profiler* profiler() { return prof_state ? &prof : nullptr; }
 };
 
@@ -621,9 +618,6 @@ int dap_create(const dap_model* mp, dap_handle** out) {
     h->d_err = nullptr;
     h->prof_state = nullptr;
     h->prof.st = nullptr;
-    h->side = nullptr;
-    h->fork_ev = nullptr;
-    h->join_ev = nullptr;
     h->h_inv_freq = build_inv_freq(m);
     hipError_t e = hipGetDevice(&h->device);
     if (e == hipSuccess) e = hipMalloc(&h->d_inv_freq, h->h_inv_freq.size() * sizeof(double));
@@ -631,9 +625,6 @@ int dap_create(const dap_model* mp, dap_handle** out) {
     if (e == hipSuccess)
         e = hipMemcpy(h->d_inv_freq, h->h_inv_freq.data(), h->h_inv_freq.size() * sizeof(double), hipMemcpyHostToDevice);
     if (e == hipSuccess) e = hipMemset(h->d_err, 0, 256);
-    if (e == hipSuccess) e = hipStreamCreateWithFlags(&h->side, hipStreamNonBlocking);   // default priority
-    if (e == hipSuccess) e = hipEventCreateWithFlags(&h->fork_ev, hipEventDisableTiming);
-    if (e == hipSuccess) e = hipEventCreateWithFlags(&h->join_ev, hipEventDisableTiming);
     if (e != hipSuccess) {
         dap_destroy(h);
         return hip_fail(e, "dap_create");
@@ -647,9 +638,6 @@ void dap_destroy(dap_handle* h) {
     delete h->prof_state;
     if (h->d_inv_freq) (void)hipFree(h->d_inv_freq);
     if (h->d_err) (void)hipFree(h->d_err);
-    if (h->fork_ev) (void)hipEventDestroy(h->fork_ev);
-    if (h->join_ev) (void)hipEventDestroy(h->join_ev);
-    if (h->side) (void)hipStreamDestroy(h->side);
     delete h;
 }
 
@@ -770,35 +758,10 @@ int dap_step_paged(dap_handle* h, const uint16_t* q, const uint16_t* k, const ui
     const size_t pre_bytes = workspace_bytes - dec_bytes;
     const uint16_t* q_step = q_out + (int64_t)n_prompt * ld_q_out;
     uint16_t* out_step = out + (int64_t)n_prompt * ld_out;
-    // With both parts present (and outside validate mode, which synchronises
-    // per call), the prompt part (its write, then the prefill) runs on the
-    // handle's second stream while the step part (its write, then the decode)
-    // runs on `stream`: the prefill's matrix work overlaps the decode's HBM
-    // streaming, and the decode waits only for its own rows' writes. Fork
-    // first, join before returning (also after an error), so the caller's
-    // stream orders everything as before.
-    if (n_prompt > 0 && n_step > 0 && !h->validate) {
-        hipError_t e = hipEventRecord(h->fork_ev, s);
-        if (e == hipSuccess) e = hipStreamWaitEvent(h->side, h->fork_ev, 0);
-        if (e != hipSuccess) return hip_fail(e, "forking the prefill stream");
-        int rc = do_write(h, q + (int64_t)n_prompt * ld_in, k + (int64_t)n_prompt * ld_in,
-                          v + (int64_t)n_prompt * ld_in, ld_in, n_step, positions + n_prompt, rows + n_prompt,
-                          slots ? slots + n_prompt : nullptr, table, table_ld, n_table_rows, q_gain, k_gain,
-                          q_out + (int64_t)n_prompt * ld_q_out, ld_q_out, k_pool, v_pool, n_pages, s);
-        if (rc == DAP_OK)
-            rc = do_write(h, q, k, v, ld_in, n_prompt, positions, rows, slots, table, table_ld, n_table_rows, q_gain,
-                          k_gain, q_out, ld_q_out, k_pool, v_pool, n_pages, h->side);
-        if (rc == DAP_OK)
-            rc = do_prefill(h, q_out, ld_q_out, n_prompt, positions, rows, n_segments, table, table_ld, n_table_rows,
-                            k_pool, v_pool, n_pages, out, ld_out, pre_ws, pre_bytes, h->side);
-        if (rc == DAP_OK)
-            rc = do_decode(h, q_step, ld_q_out, n_step, positions + n_prompt, rows + n_prompt, table, table_ld,
-                           n_table_rows, k_pool, v_pool, n_pages, out_step, ld_out, workspace, dec_bytes, s);
-        e = hipEventRecord(h->join_ev, h->side);
-        if (e == hipSuccess) e = hipStreamWaitEvent(s, h->join_ev, 0);
-        if (e != hipSuccess && rc == DAP_OK) return hip_fail(e, "joining the prefill stream");
-        return rc;
-    }
+    // Every token's write, then the prompts' prefill, then the decode, in
+    // order on `stream`. Running the prompt part on a second stream beside
+    // the decode was measured equal or slower: their workgroups cannot share
+    // a CU, so the overlap only splits the machine between them.
     int rc = do_write(h, q, k, v, ld_in, n_prompt + n_step, positions, rows, slots, table, table_ld, n_table_rows,
                       q_gain, k_gain, q_out, ld_q_out, k_pool, v_pool, n_pages, s);
     if (n_prompt > 0 && rc == DAP_OK)

@@ -194,18 +194,9 @@ int dap_attn_decode_paged(dap_handle* handle,
  * Tokens 0..n_prompt-1 are prompt tokens, tokens n_prompt..n_prompt+n_step-1
  * the decode tokens. rows[t] is every token's table row (for prompt tokens
  * also its segment); positions, rows, slots (nullable) cover all tokens.
- * Computes what writing every token first, then the packed prefill on the
- * prompt tokens and the decode on the step tokens (q read from q_out)
- * computes. With both parts present (validate mode off) the prompt part, its
- * write then its prefill, runs on a second stream the handle owns (forked
- * from and joined back to `stream` with events) while the step part, its
- * write then its decode, runs on `stream`: the prefill's matrix work overlaps
- * the decode's memory streaming. The two orders agree when no token's visible
- * keys include a slot that a token of the other part writes in the same call,
- * which holds whenever a page being written belongs to one row (rows may
- * still share read-only prefix pages). The call still orders everything on
- * `stream`. Calls on one handle must not be issued from several host threads
- * at once (the fork and join events are the handle's).
+ * Writes every token first, then runs the packed prefill on the prompt
+ * tokens and the decode on the step tokens (q read from q_out), in that
+ * order on `stream`; a token may attend slots any token of the call writes.
  * out : [n_prompt + n_step][ld_out] bf16.
  * workspace : at least dap_step_workspace_bytes() bytes of scratch.
  */

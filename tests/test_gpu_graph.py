@@ -1,8 +1,8 @@
-"""The entries under HIP graph capture: step_paged (write, the prefill on
-the handle's second stream, decode and merge) and the in-pass `packed`
-entry (index preparation, write to scratch pages, prefill) are captured
-once and replayed several times, with eager work and synchronisations
-between replays; every replay must equal the eager result bit for bit."""
+"""The entries under HIP graph capture: step_paged (write, prefill, decode
+and merge) and the in-pass `packed` entry (index preparation, write to
+scratch pages, prefill) are captured once and replayed several times, with
+eager work and synchronisations between replays; every replay must equal the
+eager result bit for bit."""
 import numpy as np
 import pytest
 import torch
