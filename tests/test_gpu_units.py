@@ -129,6 +129,28 @@ def test_prefill_unsorted_tokens_and_repeated_segments():
     check_close(to_np_bits(out), ref, "prefill shuffled")
 
 
+@pytest.mark.parametrize("n_seg", [64, 65, 5000])
+def test_prefill_many_short_segments(n_seg):
+    """One-token prompts, each its own row and tile: 64 tiles (sorted in one
+    wave's registers), 65 (sorted in LDS) and 5000 (more than the tile pass
+    sorts, dispatched in order). Each token attends its own row up to its
+    position, over pre-filled pages."""
+    model = _model(4, 2, 64, 0, max_position=256)
+    wl = _workload(model, n_seg, 4, f"pre-many-{n_seg}")
+    kp, vp = device_pools(wl)
+    rng = np.random.default_rng(n_seg)
+    pos = rng.integers(0, 256, n_seg).astype(np.int32)
+    seg = rng.permutation(n_seg).astype(np.int32)
+    q = _queries(wl, n_seg)
+    h = handle_for(model)
+    out = h.attn_prefill_packed(q, torch_i32(pos), torch_i32(seg), torch_i32(wl.table), kp, vp, n_segments=n_seg)
+    torch.cuda.synchronize()
+    op = OraclePool(wl, "cuda")
+    op.prefetch(wl.table.ravel())
+    ref = attention.paged(bf16.to_f64(to_np_bits(q)).reshape(n_seg, 4, 64), pos, seg, wl.table, op.read_page, 0)
+    check_close(to_np_bits(out), ref, f"prefill {n_seg} one-token segments")
+
+
 WRITE_MODELS = [
     _model(4, 2, 64, 0, 4096, theta=1e4),
     _model(32, 32, 96, 2047, 4096, theta=1e4),
