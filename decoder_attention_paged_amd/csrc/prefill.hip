@@ -19,8 +19,9 @@
 // Per 64-key page the workgroup stages K (key-major) and V^T (dim-major)
 // into one of two LDS buffers (one barrier per page), and each
 // wave computes S^T = K Q^T and O^T += V^T P^T with 32x32x16 bf16 MFMAs and
-// an online softmax in float32 (exp2 with the scale folded in, O rescaled
-// only when a row's running max moves). Pages fully
+// an online softmax in float32 (exp2 with the scale folded in; a row's
+// reference max, and with it O, moves only when a score passes it by more
+// than 2^8, so the weights stay at most 256). Pages fully
 // outside a wave's rows are skipped; only pages that straddle a row's causal
 // or window edge are masked element by element. Workgroups are numbered
 // kv-head-fastest so blocks sharing a kv head land on the same XCD (L2).
