@@ -151,6 +151,37 @@ def test_prefill_many_short_segments(n_seg):
     check_close(to_np_bits(out), ref, f"prefill {n_seg} one-token segments")
 
 
+def test_step_paged_decode_sees_the_prompt_written_in_the_same_call():
+    """step_paged writes every token first: a decode token that continues
+    its own row's prompt from the same call (and one that continues a prompt
+    row at the prompt's last position + 1 in another page) attends the
+    prompt's keys and values as the oracle's write-then-attend does."""
+    model = _model(8, 2, 64, 0, max_position=1024)
+    wl = _workload(model, 3, 16, "step-same-row")
+    kp, vp = device_pools(wl)
+    # row 0: prompt at 0..99, decode token at 100; row 1: prompt at 40..127
+    # (prefix 0..39 pre-filled), decode token at 128 (a new page); row 2:
+    # decode only, at 500
+    ppos = np.concatenate([np.arange(0, 100), np.arange(40, 128)]).astype(np.int32)
+    pseg = np.concatenate([np.zeros(100), np.ones(88)]).astype(np.int32)
+    dpos = np.array([100, 128, 500], np.int32)
+    drow = np.array([0, 1, 2], np.int32)
+    pos = np.concatenate([ppos, dpos])
+    rows = np.concatenate([pseg, drow])
+    T, P = len(pos), len(ppos)
+    qkv = W.normal_matrix(wl.key("qkv"), T, model.qkv_width, "cuda")
+    D, hq, hkv = model.head_dim, model.n_q_heads, model.n_kv_heads
+    h = handle_for(model)
+    q_out, out = h.step_paged(qkv[:, :hq * D], qkv[:, hq * D:(hq + hkv) * D], qkv[:, (hq + hkv) * D:],
+                              torch_i32(pos), torch_i32(rows), torch_i32(wl.table), kp, vp, n_prompt=P, n_segments=2)
+    torch.cuda.synchronize()
+    _, q_bits, k_bits, v_bits = oracle_front(wl, to_np_bits(qkv), pos, None)
+    op = OraclePool(wl, "cuda")
+    op.write(pages.slot_of(wl.table, rows, pos), k_bits, v_bits)
+    ref = attention.paged(bf16.to_f64(q_bits), pos, rows, wl.table, op.read_page, 0)
+    check_close(to_np_bits(out), ref, "step_paged over one call's own writes")
+
+
 WRITE_MODELS = [
     _model(4, 2, 64, 0, 4096, theta=1e4),
     _model(32, 32, 96, 2047, 4096, theta=1e4),
