@@ -16,9 +16,12 @@
 // and 4 below, where the softmax outweighs the matrix work per key: two
 // workgroups share a CU and, not tied by one barrier, overlap each other's
 // MFMA and VALU phases, and shorter tiles waste less at the causal diagonal.
-// Per 64-key page the workgroup stages K (key-major) and V^T (dim-major)
-// into one of two LDS buffers (one barrier per page), and each
-// wave computes S^T = K Q^T and O^T += V^T P^T with 32x32x16 bf16 MFMAs and
+// Per 64-key page the workgroup loads K and V^T straight from the pool into
+// one of 3-4 LDS buffers (buffer loads that write LDS, two or three pages
+// ahead, no registers involved), laid out as the MFMA A-operand fragments in
+// lane order so every fragment read is one contiguous kilobyte; one barrier
+// per page. Each wave computes S^T = K Q^T and O^T += V^T P^T with 32x32x16
+// bf16 MFMAs and
 // an online softmax in float32 (exp2 with the scale folded in; a row's
 // reference max, and with it O, moves only when a score passes it by more
 // than 2^8, so the weights stay at most 256). Pages fully
@@ -33,6 +36,15 @@ namespace {
 
 // waves per prefill workgroup at head_dim D
 __host__ __device__ constexpr int prefill_waves(int D) { return D >= 128 ? 8 : 4; }
+// LDS page buffers per workgroup (a page is D/4 KB): 128 KB at 128 (one
+// workgroup per CU), 72 KB at 96 and 64 KB at 64 (two per CU)
+__host__ __device__ constexpr int prefill_buffers(int D) { return D == 96 ? 3 : 4; }
+// last word of a raw buffer descriptor (32-bit data format, no swizzle)
+constexpr int kBufferWord3 = 0x00020000;
+// s_waitcnt operand: vmcnt(n), lgkmcnt(0), no wait on expcnt
+__host__ __device__ constexpr unsigned waitcnt_vmcnt(int n) {
+    return (unsigned)(n & 15) | ((unsigned)(n >> 4) << 14) | (7u << 4);
+}
 constexpr int kTilesThreads = 1024;
 constexpr int kSortTiles = 4096;       // tiles ordered longest first by the tile pass
 constexpr float kLog2e = 1.4426950408889634f;
@@ -234,6 +246,12 @@ __device__ __forceinline__ int wave_max(int v) {
     return v;
 }
 
+// One 16-byte-per-lane buffer load straight into LDS: lane l's bytes land at
+// lds + 16*l (the LDS address must be the same on every lane).
+__device__ __forceinline__ void lds_load16(__amdgpu_buffer_rsrc_t rs, u32x4* lds, int byte_offset) {
+    __builtin_amdgcn_raw_ptr_buffer_load_lds(rs, (__attribute__((address_space(3))) void*)lds, 16, byte_offset, 0, 0, 0);
+}
+
 // Key (within a 32-key S block) held in A-row i: bits 2 and 3 of i swapped,
 // so that in the 32x32 output layout lane group g's registers 8h..8h+7 are
 // the 8 contiguous keys 16h + 8g .. 16h + 8g + 7 the PV step needs.
@@ -242,18 +260,20 @@ __device__ __forceinline__ int swap23(int i) { return (i & ~12) | ((i & 4) << 1)
 template <int D, int G>
 __global__ __launch_bounds__(64 * prefill_waves(D), 8 / prefill_waves(D))
 void prefill_kernel(AttnArgs a, const int* __restrict__ tiles, int cap) {
-    constexpr int kPrefillThreads = 64 * prefill_waves(D);
     constexpr int BM = 32 * prefill_waves(D) / G;   // tokens per tile
-    constexpr int KS = D + 8;           // LDS row stride of K (elements)
-    constexpr int VS = kPage + 8;       // LDS row stride of V^T (elements)
     constexpr int kSteps = D / 16;      // QK k-steps
     constexpr int kDimBlocks = D / 32;  // PV output blocks
-    constexpr int kTileChunks = 8 * D;  // 16-byte chunks per tensor per page
-    constexpr int kChunks = (kTileChunks + kPrefillThreads - 1) / kPrefillThreads;
-    constexpr int kBufElems = kPage * KS + D * VS;
+    constexpr int W = prefill_waves(D);
+    constexpr int kFragK = 2 * kSteps;            // K fragments per page: (32-key block, k-step)
+    constexpr int kFrags = 2 * kFragK;            // and as many V^T fragments: (16-key step, dim block)
+    constexpr int kFragPerWave = kFrags / W;      // 1 KB loads per wave per page
+    constexpr int kBufBytes = kFrags * 1024;
+    constexpr int NB = prefill_buffers(D);
+    static_assert(4 * kDimBlocks == kFragK && kFrags % W == 0 && kFragK % kFragPerWave == 0, "fragment split");
 
-    // two page buffers (K then V^T in each), written and read alternately
-    extern __shared__ __attribute__((aligned(16))) uint16_t s_buf[];
+    // NB page buffers, each holding the page's K and V^T as MFMA A-operand
+    // fragments of 1 KB in lane order (lane l's 16 bytes at 16*l)
+    extern __shared__ __attribute__((aligned(1024))) u32x4 s_buf[];
 
     const int n_tiles = tiles[cap + 1];
     const int kh = blockIdx.x % a.n_kv_heads;
@@ -274,6 +294,10 @@ void prefill_kernel(AttnArgs a, const int* __restrict__ tiles, int cap) {
 
     // table row of the tile (all its tokens share the segment)
     const int trow = a.rows[t0];
+    if (a.n_pages <= 0) {                        // no page to read (every id is out of range)
+        if (tid == 0 && kh == 0) atomicOr(a.err, kErrPage);
+        return;
+    }
     if (trow < 0 || trow >= a.n_table_rows) {
         if (tid == 0 && kh == 0) atomicOr(a.err, kErrRow);
         return;
@@ -333,69 +357,86 @@ void prefill_kernel(AttnArgs a, const int* __restrict__ tiles, int cap) {
 #pragma unroll
         for (int r = 0; r < 16; ++r) o[db][r] = 0.f;
 
-    const int* tr = a.table + (long long)trow * a.table_ld;
     const int j_first = kmin >> 6;
     const int j_last = kmax >> 6;
 
-    // The row's page ids, 64 at a time in one register (lane l holds the id
-    // of page j_base + l), so the loop reads them with readlane instead of
-    // waiting on a table load after every barrier. Pages are asked for in
-    // increasing order; a new window is loaded every 64 pages.
-    int j_base = j_first;
-    int ids = j_base + lane <= j_last ? tr[j_base + lane] : -1;
-    auto page_id = [&](int j) -> int {
-        if (j - j_base >= 64) {                        // uniform
-            j_base += 64;
-            ids = j_base + lane <= j_last ? tr[j_base + lane] : -1;
-        }
-        return __builtin_amdgcn_readlane(ids, j - j_base);
+    // Page ids come by scalar loads (the table is read-only during the call):
+    // they count on lgkmcnt, so waiting for one never waits for page loads
+    // in flight. Each is loaded one page before its loads are issued.
+    typedef const __attribute__((address_space(4))) int* ConstIntPtr;
+    const ConstIntPtr trs = (ConstIntPtr)(a.table + (long long)__builtin_amdgcn_readfirstlane(trow) * a.table_ld);
+    auto page_id = [&](int j) -> int { return trs[__builtin_amdgcn_readfirstlane(j)]; };
+
+    // Each wave fills kFragPerWave of a page's fragments with 1 KB loads that
+    // go straight into LDS (lane l fetches the 16 bytes the MFMA later reads
+    // from lane l): waves 0 .. W/2-1 the K fragments, the others the V^T
+    // ones. The byte offsets inside a (page, kv head) tile are fixed per lane.
+    const int wv = __builtin_amdgcn_readfirstlane(wave);
+    const bool k_side = wv < W / 2;
+    const int f0 = (wv % (W / 2)) * kFragPerWave;      // first fragment of this wave in its tensor
+    int src_off[kFragPerWave];
+#pragma unroll
+    for (int i = 0; i < kFragPerWave; ++i) {
+        const int f = f0 + i;
+        src_off[i] = k_side ? 2 * k_tile_offset(32 * (f / kSteps) + swap23(row), 16 * (f % kSteps) + 8 * half, D)
+                            : 2 * v_tile_offset(16 * (f / kDimBlocks) + 8 * half, 32 * (f % kDimBlocks) + row, D);
+    }
+    // Loads of page pg into buffer b, issued whatever the id (an invalid one
+    // reads page 0 and is flagged), so every wave counts the same loads. They
+    // are buffer loads (counted by vmcnt alone) through a descriptor bounded
+    // to the (page, kv head) tile.
+    auto issue = [&](int pg, int b) -> bool {
+        pg = __builtin_amdgcn_readfirstlane(pg);
+        b = __builtin_amdgcn_readfirstlane(b);
+        const bool ok = pg >= 0 && pg < a.n_pages;
+        const long long tile = ((long long)(ok ? pg : 0) * a.n_kv_heads + kh) * (kPage * D);
+        const __amdgpu_buffer_rsrc_t rs = __builtin_amdgcn_make_buffer_rsrc(
+            (void*)((k_side ? a.k_pool : a.v_pool) + tile), (short)0, kPage * D * 2, kBufferWord3);
+        u32x4* dst = s_buf + b * (kBufBytes / 16) + (k_side ? 0 : 64 * kFragK) + 64 * f0;
+#pragma unroll
+        for (int i = 0; i < kFragPerWave; ++i)
+            lds_load16(rs, dst + 64 * i, src_off[i]);
+        return ok;
+    };
+    // Wait until at most `ahead` pages of this wave's loads are in flight and
+    // its LDS reads are done (loads retire in order, so the older page has landed).
+    auto wait_loads = [&](int ahead) {
+        asm volatile("" ::: "memory");
+        __builtin_amdgcn_s_waitcnt(waitcnt_vmcnt(63));   // lgkmcnt(0) on every path
+        ahead = __builtin_amdgcn_readfirstlane(ahead);   // uniform: scalar branches
+        if (NB > 3 && ahead >= 2) __builtin_amdgcn_s_waitcnt(waitcnt_vmcnt(2 * kFragPerWave));
+        else if (NB > 2 && ahead >= 1) __builtin_amdgcn_s_waitcnt(waitcnt_vmcnt(kFragPerWave));
+        else __builtin_amdgcn_s_waitcnt(waitcnt_vmcnt(0));
     };
 
-    u32x4 pk[kChunks], pv[kChunks];
-    auto prefetch = [&](int j) -> bool {
-        const int pg = page_id(j);
-        if (pg < 0 || pg >= a.n_pages) return false;
-        const uint16_t* kt = a.k_pool + ((long long)pg * a.n_kv_heads + kh) * (kPage * D);
-        const uint16_t* vt = a.v_pool + ((long long)pg * a.n_kv_heads + kh) * (kPage * D);
-#pragma unroll
-        for (int i = 0; i < kChunks; ++i) {
-            const int cidx = tid + kPrefillThreads * i;
-            if (kTileChunks % kPrefillThreads == 0 || cidx < kTileChunks) {
-                pk[i] = *reinterpret_cast<const u32x4*>(kt + 8 * cidx);
-                pv[i] = *reinterpret_cast<const u32x4*>(vt + 8 * cidx);
-            }
-        }
-        return true;
-    };
-    auto stage = [&](int buf) {
-        uint16_t* sk = s_buf + buf * kBufElems;
-        uint16_t* sv = sk + kPage * KS;
-#pragma unroll
-        for (int i = 0; i < kChunks; ++i) {
-            const int cidx = tid + kPrefillThreads * i;
-            if (kTileChunks % kPrefillThreads == 0 || cidx < kTileChunks) {
-                int key, d0, d, key0;                 // the chunk's place in the tile layout
-                k_tile_chunk(cidx, D, key, d0);
-                *reinterpret_cast<u32x4*>(&sk[key * KS + d0]) = pk[i];
-                v_tile_chunk(cidx, D, d, key0);
-                *reinterpret_cast<u32x4*>(&sv[d * VS + key0]) = pv[i];
-            }
-        }
-    };
-
-    // Pipeline: page j computes from LDS buffer (j - j_first) & 1 while page
-    // j+1's tile, prefetched into registers during page j-1, is written to
-    // the other buffer; one barrier per page.
-    bool ok_next = prefetch(j_first);
-    if (ok_next) stage(0);
-    bool ok_cur = ok_next;
-    __syncthreads();
-    if (j_first < j_last) ok_next = prefetch(j_first + 1);
+    // Pipeline over NB buffers: page j is computed from buffer (j - j_first)
+    // % NB while pages j+1 .. j+NB-1 load; the loads of page j+NB-1 start
+    // right after the barrier that ends every wave's reads of page j-1 (whose
+    // buffer they overwrite). One barrier per page.
+    unsigned okbits = 0;                 // bit k: page j+k has a valid id
+    int b_issue = 0, b_cur = 0;
+    for (int jj = j_first; jj <= j_last && jj <= j_first + NB - 2; ++jj) {
+        okbits |= (unsigned)issue(page_id(jj), b_issue) << (jj - j_first);
+        b_issue = b_issue + 1 == NB ? 0 : b_issue + 1;
+    }
+    int pg_next = j_first + NB - 1 <= j_last ? page_id(j_first + NB - 1) : -1;
 
     for (int j = j_first; j <= j_last; ++j) {
-        const int buf = (j - j_first) & 1;
-        const uint16_t* s_k = s_buf + buf * kBufElems;
-        const uint16_t* s_v = s_k + kPage * KS;
+        wait_loads(min(NB - 2, j_last - j));
+        __builtin_amdgcn_s_barrier();
+        asm volatile("" ::: "memory");
+        // every wave has read page j-1: its buffer takes the loads of page j+NB-1
+        if (j + NB - 1 <= j_last) {
+            okbits |= (unsigned)issue(pg_next, b_issue) << (NB - 1);
+            b_issue = b_issue + 1 == NB ? 0 : b_issue + 1;
+            if (j + NB <= j_last) pg_next = page_id(j + NB);
+        }
+        const bool ok_cur = okbits & 1u;
+        okbits >>= 1;
+        // fragment f of this page: fr[64 * f]; K (blk, s) is f = blk * kSteps + s,
+        // V^T (t, db) is f = kFragK + t * kDimBlocks + db
+        const u32x4* fr = s_buf + b_cur * (kBufBytes / 16) + lane;
+        b_cur = b_cur + 1 == NB ? 0 : b_cur + 1;
         const int k0 = j * kPage;
         if (!ok_cur && tid == 0 && kh == 0) atomicOr(a.err, kErrPage);
         if (ok_cur && !(k0 > w_pmax || k0 + kPage - 1 < w_lomin)) {   // skip pages invisible to this wave
@@ -405,11 +446,9 @@ void prefill_kernel(AttnArgs a, const int* __restrict__ tiles, int cap) {
         // with its MFMA, which would expose the LDS latency every time.
         u32x4 kf[2][kSteps];
 #pragma unroll
-        for (int blk = 0; blk < 2; ++blk) {
-            const uint16_t* kr = &s_k[(32 * blk + swap23(row)) * KS + 8 * half];
+        for (int blk = 0; blk < 2; ++blk)
 #pragma unroll
-            for (int s = 0; s < kSteps; ++s) kf[blk][s] = *reinterpret_cast<const u32x4*>(kr + 16 * s);
-        }
+            for (int s = 0; s < kSteps; ++s) kf[blk][s] = fr[64 * (blk * kSteps + s)];
         __builtin_amdgcn_sched_barrier(0);
         f32x16 sc[2];
 #pragma unroll
@@ -429,7 +468,7 @@ void prefill_kernel(AttnArgs a, const int* __restrict__ tiles, int cap) {
         for (int t = 0; t < 4; ++t)
 #pragma unroll
             for (int db = 0; db < kDimBlocks; ++db)
-                vfr[t][db] = *reinterpret_cast<const u32x4*>(&s_v[(32 * db + row) * VS + 16 * t + 8 * half]);
+                vfr[t][db] = fr[64 * (kFragK + t * kDimBlocks + db)];
         __builtin_amdgcn_sched_barrier(0);
         // mask where this page crosses an edge of some row's range
         if (k0 < w_lomax || k0 + kPage - 1 > w_pmin) {
@@ -487,12 +526,6 @@ void prefill_kernel(AttnArgs a, const int* __restrict__ tiles, int cap) {
         }
         lsum += ps0 + ps1;
         }
-        // next page into the other buffer (its previous contents were last read
-        // before the previous barrier), then one barrier
-        if (j < j_last && ok_next) stage(buf ^ 1);
-        ok_cur = ok_next;
-        __syncthreads();
-        if (j + 1 < j_last) ok_next = prefetch(j + 2);
     }
 
     lsum += __shfl_xor(lsum, 32);
@@ -511,7 +544,7 @@ void prefill_kernel(AttnArgs a, const int* __restrict__ tiles, int cap) {
 
 template <int D, int G>
 hipError_t launch_prefill_dg(const AttnArgs& a, int cap, const int* tiles, hipStream_t s) {
-    constexpr size_t lds = 2 * (kPage * (D + 8) + D * (kPage + 8)) * sizeof(uint16_t);
+    constexpr size_t lds = (size_t)prefill_buffers(D) * (D / 4) * 1024;
     static bool configured = false;     // raise the dynamic LDS limit once per instantiation
     if (!configured) {
         hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void*>(&prefill_kernel<D, G>),
