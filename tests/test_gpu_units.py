@@ -151,6 +151,51 @@ def test_prefill_many_short_segments(n_seg):
     check_close(to_np_bits(out), ref, f"prefill {n_seg} one-token segments")
 
 
+@pytest.mark.parametrize("d,hq,hkv", [(64, 4, 2), (96, 4, 4), (128, 8, 2)])
+@pytest.mark.parametrize("n_pages", [1, 2, 3, 4, 5, 6])
+def test_prefill_tile_of_n_pages(d, hq, hkv, n_pages):
+    """One tile of 64 tokens at positions 64(n-1) .. 64n-1 attends exactly n
+    pages: fewer, as many and more pages than the kernel keeps in flight (its
+    LDS ring holds 3 pages at head_dim 96 and 4 otherwise), so the pipeline's
+    start, steady state and drain are each exercised."""
+    model = _model(hq, hkv, d, 0, max_position=512)
+    wl = _workload(model, 1, 6, f"pre-npages-{d}-{n_pages}")
+    kp, vp = device_pools(wl)
+    pos = np.arange(64 * (n_pages - 1), 64 * n_pages, dtype=np.int32)
+    seg = np.zeros(64, np.int32)
+    q = _queries(wl, 64)
+    h = handle_for(model)
+    out = h.attn_prefill_packed(q, torch_i32(pos), torch_i32(seg), torch_i32(wl.table), kp, vp, n_segments=1)
+    torch.cuda.synchronize()
+    op = OraclePool(wl, "cuda")
+    op.prefetch(wl.table.ravel())
+    ref = attention.paged(bf16.to_f64(to_np_bits(q)).reshape(64, hq, d), pos, seg, wl.table, op.read_page, 0)
+    check_close(to_np_bits(out), ref, f"prefill tile of {n_pages} pages, head_dim {d}")
+
+
+def test_prefill_out_of_range_page_is_skipped_and_other_segments_are_untouched():
+    """Without validate mode a page id past the pool is caught by the kernel:
+    that page is neither read nor attended, and the segments whose rows are
+    sound match the oracle."""
+    model = _model(8, 2, 128, 0, max_position=512)
+    wl = _workload(model, 3, 4, "pre-bad-page")
+    kp, vp = device_pools(wl)
+    bad = wl.table.copy()
+    bad[1, 1] = 1 << 30
+    pos = np.tile(np.arange(100, 200, dtype=np.int32), 3)
+    seg = np.repeat(np.arange(3, dtype=np.int32), 100)
+    q = _queries(wl, 300)
+    h = handle_for(model)
+    out = h.attn_prefill_packed(q, torch_i32(pos), torch_i32(seg), torch_i32(bad), kp, vp, n_segments=3)
+    torch.cuda.synchronize()
+    op = OraclePool(wl, "cuda")
+    op.prefetch(wl.table.ravel())
+    good = seg != 1
+    ref = attention.paged(bf16.to_f64(to_np_bits(q)).reshape(300, 8, 128)[good], pos[good], seg[good], wl.table,
+                          op.read_page, 0)
+    check_close(to_np_bits(out)[good], ref, "segments beside the bad page id")
+
+
 def test_step_paged_decode_sees_the_prompt_written_in_the_same_call():
     """step_paged writes every token first: a decode token that continues
     its own row's prompt from the same call (and one that continues a prompt
