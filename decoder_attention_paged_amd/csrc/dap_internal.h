@@ -48,20 +48,6 @@ __host__ __device__ __forceinline__ int v_tile_offset(int key, int d, int D) {
     const int f = half * (D / 16) + (d >> 4);
     return ((f * 64 + (kk >> 3) * 16 + (d & 15)) << 3) + (kk & 7);
 }
-// the 8 elements of 16-byte chunk c: K row `key` dims d0..d0+7; V dim `d`
-// keys key0..key0+7
-__host__ __device__ __forceinline__ void k_tile_chunk(int c, int D, int& key, int& d0) {
-    const int f = c >> 6, l = c & 63;
-    const int hb = f / (D / 32), s = f % (D / 32);
-    key = 32 * (hb >> 1) + unit_key(hb & 1, l & 15);
-    d0 = 32 * s + 8 * (l >> 4);
-}
-__host__ __device__ __forceinline__ void v_tile_chunk(int c, int D, int& d, int& key0) {
-    const int f = c >> 6, l = c & 63;
-    const int half = f / (D / 16), db = f % (D / 16);
-    d = 16 * db + (l & 15);
-    key0 = 32 * half + 8 * (l >> 4);
-}
 
 typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
 typedef float f32x4 __attribute__((ext_vector_type(4)));
