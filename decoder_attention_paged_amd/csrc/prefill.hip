@@ -28,6 +28,8 @@
 // outside a wave's rows are skipped; only pages that straddle a row's causal
 // or window edge are masked element by element. Workgroups are numbered
 // kv-head-fastest so blocks sharing a kv head land on the same XCD (L2).
+#include <atomic>
+
 #include "dap_internal.h"
 
 namespace dap {
@@ -545,12 +547,19 @@ void prefill_kernel(AttnArgs a, const int* __restrict__ tiles, int cap) {
 template <int D, int G>
 hipError_t launch_prefill_dg(const AttnArgs& a, int cap, const int* tiles, hipStream_t s) {
     constexpr size_t lds = (size_t)prefill_buffers(D) * (D / 4) * 1024;
-    static bool configured = false;     // raise the dynamic LDS limit once per instantiation
-    if (!configured) {
-        hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void*>(&prefill_kernel<D, G>),
-                                           hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds);
+    // The dynamic LDS limit is raised once per device (the attribute is per
+    // device); bit d of `configured` records device d. Devices past 63 set
+    // it on every launch.
+    static std::atomic<unsigned long long> configured{0};
+    int dev = 0;
+    hipError_t e = hipGetDevice(&dev);
+    if (e != hipSuccess) return e;
+    const unsigned long long bit = dev < 64 ? 1ull << dev : 0ull;
+    if (!(configured.load(std::memory_order_acquire) & bit)) {
+        e = hipFuncSetAttribute(reinterpret_cast<const void*>(&prefill_kernel<D, G>),
+                                hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds);
         if (e != hipSuccess) return e;
-        configured = true;
+        configured.fetch_or(bit, std::memory_order_release);
     }
     hipLaunchKernelGGL((prefill_kernel<D, G>), dim3((unsigned)cap * a.n_kv_heads), dim3(64 * prefill_waves(D)), lds,
                        s, a, tiles, cap);
