@@ -120,16 +120,13 @@ __global__ __launch_bounds__(kTilesThreads) void prefill_tiles_kernel(const int3
     const bool masked = chunk <= 64;
     auto starts_run = [&](int t) { return t == 0 || seg[t] != seg[t - 1]; };
 
-    // run starts of my chunk; the last one
+    // run starts of my chunk; the last one. Chunks of 8 ids or more whose
+    // ids are 16-byte aligned are read with 16-byte loads, 8 ids at a time,
+    // the id before each group carried from the group before; shorter ones
+    // 8 (or fewer) single ids at a time.
     unsigned long long flags = 0ull;
     int my_start = -1;
-    for (int b = c0; b < c1; b += 8) {
-        int v[9];
-#pragma unroll
-        for (int i = 0; i < 9; ++i) {
-            const int t = b - 1 + i;
-            v[i] = t >= 0 && t < c1 ? seg[t] : 0;
-        }
+    auto mark = [&](const int* v, int b) {
 #pragma unroll
         for (int i = 1; i < 9; ++i) {
             const int t = b - 1 + i;
@@ -137,6 +134,37 @@ __global__ __launch_bounds__(kTilesThreads) void prefill_tiles_kernel(const int3
                 my_start = t;
                 if (masked) flags |= 1ull << (t - c0);
             }
+        }
+    };
+    auto load_scalar = [&](int* v, int b) {
+#pragma unroll
+        for (int i = 0; i < 9; ++i) {
+            const int t = b - 1 + i;
+            v[i] = t >= 0 && t < c1 ? seg[t] : 0;
+        }
+    };
+    if ((reinterpret_cast<uintptr_t>(seg) & 15) == 0 && (chunk & 3) == 0 && chunk >= 8) {
+        int prev = 0;
+#pragma unroll 4
+        for (int b = c0; b < c1; b += 8) {
+            int v[9];
+            if (b + 8 <= c1) {
+                v[0] = b > c0 ? prev : (b > 0 ? seg[b - 1] : 0);
+                const int4 x = *reinterpret_cast<const int4*>(seg + b);
+                const int4 y = *reinterpret_cast<const int4*>(seg + b + 4);
+                v[1] = x.x; v[2] = x.y; v[3] = x.z; v[4] = x.w;
+                v[5] = y.x; v[6] = y.y; v[7] = y.z; v[8] = y.w;
+            } else {
+                load_scalar(v, b);
+            }
+            mark(v, b);
+            prev = v[8];
+        }
+    } else {
+        for (int b = c0; b < c1; b += 8) {
+            int v[9];
+            load_scalar(v, b);
+            mark(v, b);
         }
     }
     auto is_start = [&](int t) { return masked ? ((flags >> (t - c0)) & 1ull) != 0 : starts_run(t); };
