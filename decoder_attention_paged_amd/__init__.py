@@ -119,6 +119,51 @@ def _ptr(t: Optional[torch.Tensor]):
     return None if t is None else ctypes.c_void_p(t.data_ptr())
 
 
+# Extents the C side cannot see: it receives pointers and the sizes derived
+# here, so a short or misplaced tensor is refused before any kernel reads it.
+def _need(cond: bool, msg: str):
+    if not cond:
+        raise DapError(INVALID_ARG, msg)
+
+
+def _on_gpu(name: str, t: torch.Tensor):
+    _need(t.is_cuda, f"{name} must be a GPU tensor")
+
+
+def _mat(name: str, t: Optional[torch.Tensor], n: int, width: int):
+    """A 2-D GPU tensor with at least n rows of at least width columns."""
+    if t is None:
+        return
+    _on_gpu(name, t)
+    _need(t.dim() == 2 and t.shape[0] >= n and t.shape[1] >= width,
+          f"{name}: expected at least [{n}, {width}], got {list(t.shape)}")
+
+
+def _vec(name: str, t: Optional[torch.Tensor], n: int):
+    """A 1-D GPU tensor with at least n entries."""
+    if t is None:
+        return
+    _on_gpu(name, t)
+    _need(t.dim() == 1 and t.shape[0] >= n, f"{name}: expected at least {n} entries, got {list(t.shape)}")
+
+
+def _pools(m: "Model", k_pool: torch.Tensor, v_pool: torch.Tensor, min_pages: int = 1):
+    """Contiguous [n_pages, Hkv, 64 * D] pools of the same size."""
+    per_page = m.n_kv_heads * m.page_size * m.head_dim
+    for name, t in (("k_pool", k_pool), ("v_pool", v_pool)):
+        _on_gpu(name, t)
+        _need(t.dim() >= 1 and t.is_contiguous() and t.shape[0] >= min_pages and t.numel() == t.shape[0] * per_page,
+              f"{name}: expected a contiguous [n_pages >= {min_pages}, {m.n_kv_heads}, {m.page_size * m.head_dim}] "
+              f"pool, got {list(t.shape)}")
+    _need(k_pool.shape[0] == v_pool.shape[0], "k_pool and v_pool must hold the same number of pages")
+
+
+def _table(t: Optional[torch.Tensor]):
+    if t is not None:
+        _on_gpu("table", t)
+        _need(t.dim() == 2, f"table: expected [rows, table_ld], got {list(t.shape)}")
+
+
 def _stream(stream):
     if stream is None:
         stream = torch.cuda.current_stream()
@@ -225,6 +270,7 @@ class Handle:
         once); otherwise a zeroed one is allocated for this call."""
         if ws is None:
             ws = torch.zeros(max(nbytes, 16), dtype=torch.uint8, device=like.device)
+        _on_gpu("workspace", ws)
         return ws
 
     def workspace(self, nbytes: int, device="cuda") -> torch.Tensor:
@@ -240,6 +286,7 @@ class Handle:
         T = positions.shape[0]
         if q_out is None:
             q_out = torch.empty(T, m.n_q_heads * m.head_dim, dtype=q.dtype, device=q.device)
+        self._check_tokens(T, q, k, v, positions, (rows, slots), q_gain, k_gain, q_out, k_pool, v_pool, table)
         ld = _ld(q)
         if _ld(k) != ld or _ld(v) != ld:
             raise ValueError("q, k and v must share one row stride")
@@ -260,6 +307,7 @@ class Handle:
             n_segments = T
         if out is None:
             out = torch.empty(T, m.n_q_heads * m.head_dim, dtype=q.dtype, device=q.device)
+        self._check_attn(T, q, positions, segments, out, k_pool, v_pool, table)
         nb = self.prefill_workspace_bytes(T, n_segments)
         ws = self._workspace(workspace, nb, q)
         _check(_lib.dap_attn_prefill_packed(
@@ -275,6 +323,7 @@ class Handle:
         R = positions.shape[0]
         if out is None:
             out = torch.empty(R, m.n_q_heads * m.head_dim, dtype=q.dtype, device=q.device)
+        self._check_attn(R, q, positions, rows, out, k_pool, v_pool, table)
         nb = self.decode_workspace_bytes(R)
         ws = self._workspace(workspace, nb, q)
         _check(_lib.dap_attn_decode_paged(
@@ -294,6 +343,8 @@ class Handle:
             q_out = torch.empty(T, m.n_q_heads * m.head_dim, dtype=q.dtype, device=q.device)
         if out is None:
             out = torch.empty(T, m.n_q_heads * m.head_dim, dtype=q.dtype, device=q.device)
+        self._check_tokens(T, q, k, v, positions, (rows, slots), q_gain, k_gain, q_out, k_pool, v_pool, table)
+        _mat("out", out, T, m.n_q_heads * m.head_dim)
         nb = self.step_workspace_bytes(n_prompt, n_segments, n_step)
         ws = self._workspace(workspace, nb, q)
         ld = _ld(q)
@@ -311,6 +362,34 @@ class Handle:
     def cache_workspace_bytes(self, n_tokens: int, n_groups: int, cache_rows: int, max_seq: int) -> int:
         return int(_lib.dap_cache_workspace_bytes(self._h, n_tokens, n_groups, cache_rows, max_seq))
 
+    def _check_tokens(self, T, q, k, v, positions, index_arrays, q_gain, k_gain, q_out, k_pool=None, v_pool=None,
+                      table=None, min_pages=1):
+        m = self.model
+        _vec("positions", positions, T)
+        _mat("q", q, T, m.n_q_heads * m.head_dim)
+        _mat("k", k, T, m.n_kv_heads * m.head_dim)
+        _mat("v", v, T, m.n_kv_heads * m.head_dim)
+        for t in index_arrays:
+            _vec("rows/slots/segments", t, T)
+        _vec("q_gain", q_gain, m.head_dim)
+        _vec("k_gain", k_gain, m.head_dim)
+        _mat("q_out/out", q_out, T, m.n_q_heads * m.head_dim)
+        if k_pool is not None:
+            _pools(m, k_pool, v_pool, min_pages)
+        _table(table)
+
+    def _check_attn(self, T, q, positions, index, out, k_pool, v_pool, table):
+        m = self.model
+        _vec("positions", positions, T)
+        _mat("q", q, T, m.n_q_heads * m.head_dim)
+        _vec("rows/segments", index, T)
+        _mat("out", out, T, m.n_q_heads * m.head_dim)
+        _pools(m, k_pool, v_pool)
+        _table(table)
+
+    def _cache_pages(self, cache_rows, max_seq):
+        return -(-cache_rows * max_seq // self.model.page_size)
+
     def _qkv(self, q, k, v):
         ld = _ld(q)
         if _ld(k) != ld or _ld(v) != ld:
@@ -327,6 +406,8 @@ class Handle:
         cache_rows * max_seq / 64 pages, row r owning pages r*max_seq/64 onward."""
         R = q.shape[0]
         out = self._out(out, R, q)
+        self._check_tokens(R, q, k, v, None, (), q_gain, k_gain, out, k_pool, v_pool,
+                           min_pages=self._cache_pages(R, max_seq))
         ws = self._workspace(workspace, self.cache_workspace_bytes(R, 1, R, max_seq), q)
         _check(_lib.dap_decode(self._h, *self._qkv(q, k, v), R, pos, max_seq, _ptr(_bf16(q_gain)),
                                _ptr(_bf16(k_gain)), _ptr(_bf16(k_pool)), _ptr(_bf16(v_pool)), _ptr(_bf16(out)),
@@ -338,6 +419,8 @@ class Handle:
         """One token per cache row, row b at positions[b]."""
         R = q.shape[0]
         out = self._out(out, R, q)
+        self._check_tokens(R, q, k, v, positions, (), q_gain, k_gain, out, k_pool, v_pool,
+                           min_pages=self._cache_pages(R, max_seq))
         ws = self._workspace(workspace, self.cache_workspace_bytes(R, 1, R, max_seq), q)
         _check(_lib.dap_decode_rows(self._h, *self._qkv(q, k, v), R, _ptr(_i32(positions)), max_seq,
                                     _ptr(_bf16(q_gain)), _ptr(_bf16(k_gain)), _ptr(_bf16(k_pool)),
@@ -351,6 +434,8 @@ class Handle:
         T = q.shape[0]
         seq = T // cache_rows
         out = self._out(out, T, q)
+        self._check_tokens(T, q, k, v, None, (), q_gain, k_gain, out, k_pool, v_pool,
+                           min_pages=self._cache_pages(cache_rows, max_seq))
         ws = self._workspace(workspace, self.cache_workspace_bytes(T, cache_rows, cache_rows, max_seq), q)
         _check(_lib.dap_prefill(self._h, *self._qkv(q, k, v), cache_rows, seq, pos, max_seq, _ptr(_bf16(q_gain)),
                                 _ptr(_bf16(k_gain)), _ptr(_bf16(k_pool)), _ptr(_bf16(v_pool)), _ptr(_bf16(out)),
@@ -363,6 +448,9 @@ class Handle:
         T = q.shape[0]
         M = slots.shape[0]
         out = self._out(out, T, q)
+        self._check_tokens(T, q, k, v, None, (), q_gain, k_gain, out, k_pool, v_pool,
+                           min_pages=self._cache_pages(cache_rows, max_seq))
+        _vec("slots", slots, M)
         ws = self._workspace(workspace, self.cache_workspace_bytes(T, M, cache_rows, max_seq), q)
         _check(_lib.dap_prefill_slots(self._h, *self._qkv(q, k, v), M, T // M, _ptr(_i32(slots)), cache_rows,
                                       max_seq, _ptr(_bf16(q_gain)), _ptr(_bf16(k_gain)), _ptr(_bf16(k_pool)),
@@ -379,6 +467,7 @@ class Handle:
         """Attention among the call's tokens: same segment, earlier or equal position."""
         T = positions.shape[0]
         out = self._out(out, T, q)
+        self._check_tokens(T, q, k, v, positions, (segments,), q_gain, k_gain, out)
         ws = self._workspace(workspace, self.inpass_workspace_bytes(T, n_segments), q)
         _check(_lib.dap_packed(self._h, *self._qkv(q, k, v), T, _ptr(_i32(positions)), _ptr(_i32(segments)),
                                n_segments, _ptr(_bf16(q_gain)), _ptr(_bf16(k_gain)), _ptr(_bf16(out)), _ld(out),
@@ -389,6 +478,7 @@ class Handle:
         """n_seqs sequences of T/n_seqs tokens from position 0, no cache."""
         T = q.shape[0]
         out = self._out(out, T, q)
+        self._check_tokens(T, q, k, v, None, (), q_gain, k_gain, out)
         ws = self._workspace(workspace, self.inpass_workspace_bytes(T, n_seqs), q)
         _check(_lib.dap_forward(self._h, *self._qkv(q, k, v), n_seqs, T // n_seqs, _ptr(_bf16(q_gain)),
                                 _ptr(_bf16(k_gain)), _ptr(_bf16(out)), _ld(out), _ptr(ws), ws.numel(),

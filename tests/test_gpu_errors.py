@@ -77,13 +77,47 @@ def test_argument_checks():
         h.attn_decode_paged(q, pos, table, kp, vp, out=q)
     assert e.value.status == dap.INVALID_ARG
     with pytest.raises(dap.DapError) as e:                        # row stride not a multiple of 8
-        h.attn_decode_paged(torch.empty(4, 1028, dtype=torch.int16, device="cuda")[:, :1020], pos, table, kp, vp)
+        h.attn_decode_paged(torch.empty(4, 1028, dtype=torch.int16, device="cuda")[:, :1024], pos, table, kp, vp)
     assert e.value.status == dap.INVALID_ARG
     g = handle_for(W.ModelShape("g8", 16, 2, 128, 1e4, max_position=512))   # group 8: decode only
     with pytest.raises(dap.DapError) as e:
         g.attn_prefill_packed(torch.zeros(4, 2048, dtype=torch.int16, device="cuda"), torch_i32([0, 1, 2, 3]),
                               torch_i32([0, 0, 0, 0]), table, kp, vp, n_segments=1)
     assert e.value.status == dap.UNSUPPORTED
+
+
+def test_binding_refuses_tensors_the_kernels_would_overrun():
+    """The C side sees pointers and the sizes the binding derives; tensors
+    that are too short, on the host, or shaped for another model are refused
+    before any kernel runs."""
+    wl, m, kp, vp = _setup()
+    h = handle_for(m)
+    width = m.n_q_heads * m.head_dim
+    q = W.normal_matrix(wl.key("q"), 4, width, "cuda")
+    pos = torch_i32([10, 200, 511, 64])
+    table = torch_i32(wl.table)
+    bad_calls = {
+        "q on the host": lambda: h.attn_decode_paged(q.cpu(), pos, table, kp, vp),
+        "q with fewer rows than positions": lambda: h.attn_decode_paged(q[:3], pos, table, kp, vp),
+        "q narrower than Hq*D": lambda: h.attn_decode_paged(q[:, :width - 8], pos, table, kp, vp),
+        "out with fewer rows": lambda: h.attn_decode_paged(q, pos, table, kp, vp, out=torch.empty_like(q)[:2]),
+        "pool for another kv head count": lambda: h.attn_decode_paged(q, pos, table, kp.view(-1, 1, kp.shape[-1]),
+                                                                      vp.view(-1, 1, vp.shape[-1])),
+        "pools of different sizes": lambda: h.attn_decode_paged(q, pos, table, kp, vp[:-1]),
+        "segments shorter than the tokens": lambda: h.attn_prefill_packed(q, pos, pos[:2], table, kp, vp,
+                                                                         n_segments=4),
+        "table on the host": lambda: h.attn_decode_paged(q, pos, table.cpu(), kp, vp),
+        "workspace on the host": lambda: h.attn_decode_paged(q, pos, table, kp, vp,
+                                                            workspace=torch.zeros(1 << 20, dtype=torch.uint8)),
+        "cache pool smaller than rows x max_seq": lambda: h.decode(q, q[:, :m.n_kv_heads * m.head_dim],
+                                                                   q[:, :m.n_kv_heads * m.head_dim], 5, kp, vp,
+                                                                   max_seq=kp.shape[0] * 64),
+    }
+    for what, call in bad_calls.items():
+        with pytest.raises(dap.DapError) as e:
+            call()
+        assert e.value.status == dap.INVALID_ARG, what
+    torch.cuda.synchronize()
 
 
 def test_empty_calls_are_no_ops():
