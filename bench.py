@@ -512,7 +512,7 @@ def main():
     ap.add_argument("--no-cpu-baseline", action="store_true")
     args = ap.parse_args()
     if args.gpus != 1:
-        print(f"bench.py runs on one GPU only: this build has no multi-GPU path (asked for --gpus {args.gpus}); "
+        print(f"bench.py runs on one GPU only: the library has no multi-GPU path (asked for --gpus {args.gpus}); "
               "the core would shard by kv head with no exchange, see the design notes", file=sys.stderr)
         sys.exit(2)
     if not torch.cuda.is_available():
