@@ -179,14 +179,14 @@ class Bench:
                                   torch.empty(len(rows), hq * D, dtype=torch.int16, device="cuda")))
                 self.dec_bytes += decode_bytes(m, positions)
                 n_tok += len(rows)
-            self.ws = self.h.workspace(self.h.decode_workspace_bytes(4))
+            self.ws = self.h.workspace(self.h.step_workspace_bytes(0, 1, 4))
             self.bytes = write_bytes(m, n_tok) + self.dec_bytes
             self.flops = 0.0
             self.tokens = n_tok
             self.qkv = qkv
             self.desc = ("phi-3-mini-shaped decode loop: 2489 steps (7908 row-steps) from each prompt end to position "
-                         "3000, window 2047, Hq=Hkv=32, D96; a write and a decode per step, the loop captured as one "
-                         "HIP graph and replayed")
+                         "3000, window 2047, Hq=Hkv=32, D96; one step_paged call per step (each row's new token "
+                         "written and attended), the loop captured as one HIP graph and replayed")
             torch.cuda.synchronize()
             self.step_eager()
             torch.cuda.synchronize()
@@ -241,12 +241,10 @@ class Bench:
     def step_eager(self):
         h, m, wl = self.h, self.m, self.wl
         if self.name == "phi3_loop":
+            W_q, W_k = m.n_q_heads * m.head_dim, m.n_kv_heads * m.head_dim
             for x, tp, tr, qo, o in self.loop:
-                h.rope_qknorm_write_pages(x[:, :m.n_q_heads * m.head_dim],
-                                          x[:, m.n_q_heads * m.head_dim:(m.n_q_heads + m.n_kv_heads) * m.head_dim],
-                                          x[:, (m.n_q_heads + m.n_kv_heads) * m.head_dim:], tp, self.kp, self.vp,
-                                          rows=tr, table=self.table, q_out=qo)
-                h.attn_decode_paged(qo, tp, self.table, self.kp, self.vp, rows=tr, out=o, workspace=self.ws)
+                h.step_paged(x[:, :W_q], x[:, W_q:W_q + W_k], x[:, W_q + W_k:], tp, tr, self.table, self.kp, self.vp,
+                             n_prompt=0, n_segments=1, q_out=qo, out=o, workspace=self.ws)
             return
         if self.name == "qwen3":
             h.step_paged(*self.split, self.pos, self.rows, self.table, self.kp, self.vp, n_prompt=wl.n_pre,

@@ -205,13 +205,16 @@ dap::AttnArgs attn_args(dap_handle* h, const uint16_t* q, int64_t ld_q, int32_t 
 }
 
 // ---------------------------------------------------------------- entry bodies
-int do_write(dap_handle* h, const uint16_t* q, const uint16_t* k, const uint16_t* v, int64_t ld_in,
-             int32_t n_tokens, const int32_t* positions, const int32_t* rows, const int32_t* slots,
-             const int32_t* table, int32_t table_ld, int32_t n_table_rows, const uint16_t* q_gain,
-             const uint16_t* k_gain, uint16_t* q_out, int64_t ld_q_out, uint16_t* k_pool, uint16_t* v_pool,
-             int32_t n_pages, hipStream_t s) {
+// Argument checks of a write of n_tokens (and, in validate mode, the
+// host-side index checks); fills `a`. Nothing is launched.
+int write_args(dap_handle* h, const uint16_t* q, const uint16_t* k, const uint16_t* v, int64_t ld_in,
+               int32_t n_tokens, const int32_t* positions, const int32_t* rows, const int32_t* slots,
+               const int32_t* table, int32_t table_ld, int32_t n_table_rows, const uint16_t* q_gain,
+               const uint16_t* k_gain, uint16_t* q_out, int64_t ld_q_out, uint16_t* k_pool, uint16_t* v_pool,
+               int32_t n_pages, dap::WriteArgs& a, hipStream_t s) {
     const dap_model& m = h->m;
     const int64_t D = m.head_dim;
+    a = dap::WriteArgs{};
     DAP_REQUIRE(n_tokens >= 0, DAP_INVALID_ARG, "n_tokens must be >= 0");
     if (n_tokens == 0) return DAP_OK;
     DAP_REQUIRE(q && k && v && q_out && k_pool && v_pool, DAP_INVALID_ARG, "null tensor pointer");
@@ -251,18 +254,35 @@ int do_write(dap_handle* h, const uint16_t* q, const uint16_t* k, const uint16_t
         std::unordered_set<long long> seen;
         for (long long x : sl)
             if (!seen.insert(x).second) return fail(DAP_BAD_INDEX, "two tokens write the same slot " + std::to_string(x));
-        if (int rc = begin_validate(h, s)) return rc;
     }
-    dap::WriteArgs a;
     a.q = q; a.k = k; a.v = v; a.ld_in = ld_in; a.n_tokens = n_tokens; a.positions = positions;
     a.rows = rows; a.slots = slots; a.table = table; a.table_ld = table_ld; a.n_table_rows = n_table_rows;
     a.q_gain = q_gain; a.k_gain = k_gain; a.q_out = q_out; a.ld_q_out = ld_q_out;
     a.k_pool = k_pool; a.v_pool = v_pool; a.n_pages = n_pages;
     a.n_q_heads = m.n_q_heads; a.n_kv_heads = m.n_kv_heads; a.head_dim = m.head_dim; a.max_position = m.max_position;
     a.qk_norm = m.qk_norm; a.eps = m.qk_norm_eps; a.inv_freq = h->d_inv_freq; a.err = h->d_err;
+    return DAP_OK;
+}
+
+int launch_write_checked(dap_handle* h, const dap::WriteArgs& a, hipStream_t s) {
+    if (a.n_tokens == 0) return DAP_OK;
+    if (h->validate)
+        if (int rc = begin_validate(h, s)) return rc;
     hipError_t e = dap::launch_write(a, s, h->profiler());
     if (e != hipSuccess) return hip_fail(e, "rope/write launch");
     return h->validate ? end_validate(h, s) : DAP_OK;
+}
+
+int do_write(dap_handle* h, const uint16_t* q, const uint16_t* k, const uint16_t* v, int64_t ld_in,
+             int32_t n_tokens, const int32_t* positions, const int32_t* rows, const int32_t* slots,
+             const int32_t* table, int32_t table_ld, int32_t n_table_rows, const uint16_t* q_gain,
+             const uint16_t* k_gain, uint16_t* q_out, int64_t ld_q_out, uint16_t* k_pool, uint16_t* v_pool,
+             int32_t n_pages, hipStream_t s) {
+    dap::WriteArgs a;
+    if (int rc = write_args(h, q, k, v, ld_in, n_tokens, positions, rows, slots, table, table_ld, n_table_rows,
+                            q_gain, k_gain, q_out, ld_q_out, k_pool, v_pool, n_pages, a, s))
+        return rc;
+    return launch_write_checked(h, a, s);
 }
 
 int attn_common_checks(dap_handle* h, const uint16_t* q, int64_t ld_q, const int32_t* positions, const int32_t* table,
@@ -318,7 +338,7 @@ int do_prefill(dap_handle* h, const uint16_t* q, int64_t ld_q, int32_t n_tokens,
 int do_decode(dap_handle* h, const uint16_t* q, int64_t ld_q, int32_t n_rows, const int32_t* positions,
               const int32_t* rows, const int32_t* table, int32_t table_ld, int32_t n_table_rows,
               const uint16_t* k_pool, const uint16_t* v_pool, int32_t n_pages, uint16_t* out, int64_t ld_out,
-              void* workspace, size_t workspace_bytes, hipStream_t s) {
+              void* workspace, size_t workspace_bytes, hipStream_t s, const dap::WriteArgs* fused = nullptr) {
     DAP_REQUIRE(n_rows >= 0, DAP_INVALID_ARG, "n_rows must be >= 0");
     if (n_rows == 0) return DAP_OK;
     DAP_REQUIRE(n_rows <= dap::kMaxDecodeRows, DAP_UNSUPPORTED, "at most 65535 rows per decode call");
@@ -341,7 +361,7 @@ int do_decode(dap_handle* h, const uint16_t* q, int64_t ld_q, int32_t n_rows, co
     }
     dap::AttnArgs a = attn_args(h, q, ld_q, n_rows, positions, rows, table, table_ld, n_table_rows, k_pool, v_pool,
                                 n_pages, out, ld_out);
-    hipError_t e = dap::launch_decode(a, plan, workspace, s, h->profiler());
+    hipError_t e = dap::launch_decode(a, plan, workspace, s, h->profiler(), fused);
     if (e != hipSuccess) return hip_fail(e, "decode launch");
     return h->validate ? end_validate(h, s) : DAP_OK;
 }
@@ -758,18 +778,46 @@ int dap_step_paged(dap_handle* h, const uint16_t* q, const uint16_t* k, const ui
     const size_t pre_bytes = workspace_bytes - dec_bytes;
     const uint16_t* q_step = q_out + (int64_t)n_prompt * ld_q_out;
     uint16_t* out_step = out + (int64_t)n_prompt * ld_out;
-    // Every token's write, then the prompts' prefill, then the decode, in
-    // order on `stream`. Running the prompt part on a second stream beside
-    // the decode was measured equal or slower: their workgroups cannot share
-    // a CU, so the overlap only splits the machine between them.
-    int rc = do_write(h, q, k, v, ld_in, n_prompt + n_step, positions, rows, slots, table, table_ld, n_table_rows,
-                      q_gain, k_gain, q_out, ld_q_out, k_pool, v_pool, n_pages, s);
+    dap::WriteArgs wa;
+    if (int rc = write_args(h, q, k, v, ld_in, n_prompt + n_step, positions, rows, slots, table, table_ld,
+                            n_table_rows, q_gain, k_gain, q_out, ld_q_out, k_pool, v_pool, n_pages, wa, s))
+        return rc;
+    // In order on `stream`: every token's write, the prompts' prefill, then
+    // the decode. (The prompt part on a second stream beside the decode was
+    // measured equal or slower: their workgroups cannot share a CU.) A call
+    // with no prompt tokens skips the write launch: the decode writes each
+    // row's token itself (K, V and q_out, from the workgroup that reads the
+    // token's page) before reading it. That needs q_out apart from q (the
+    // decode's workgroups read q while q_out is written).
+    const bool fused = n_prompt == 0 && n_step > 0 && q_out != q;
+    if (fused && h->validate) {
+        std::vector<int32_t> hr;
+        if (!to_host(hr, rows, n_step, s)) return fail(DAP_HIP_ERROR, "copying rows");
+        std::unordered_set<int32_t> step_rows;
+        for (int t = 0; t < n_step; ++t)
+            if (!step_rows.insert(hr[t]).second)
+                return fail(DAP_BAD_INDEX, "two step tokens in row " + std::to_string(hr[t]));
+    }
+    dap::WriteArgs wp = wa;
+    if (fused) wp.n_tokens = n_prompt;
+    int rc = launch_write_checked(h, wp, s);
     if (n_prompt > 0 && rc == DAP_OK)
         rc = do_prefill(h, q_out, ld_q_out, n_prompt, positions, rows, n_segments, table, table_ld, n_table_rows,
                         k_pool, v_pool, n_pages, out, ld_out, pre_ws, pre_bytes, s);
-    if (n_step > 0 && rc == DAP_OK)
+    if (n_step > 0 && rc == DAP_OK) {
+        dap::WriteArgs wd = wa;
+        wd.q += n_prompt * ld_in;
+        wd.k += n_prompt * ld_in;
+        wd.v += n_prompt * ld_in;
+        wd.positions += n_prompt;
+        wd.rows += n_prompt;
+        if (wd.slots) wd.slots += n_prompt;
+        wd.q_out += n_prompt * ld_q_out;
+        wd.n_tokens = n_step;
         rc = do_decode(h, q_step, ld_q_out, n_step, positions + n_prompt, rows + n_prompt, table, table_ld,
-                       n_table_rows, k_pool, v_pool, n_pages, out_step, ld_out, workspace, dec_bytes, s);
+                       n_table_rows, k_pool, v_pool, n_pages, out_step, ld_out, workspace, dec_bytes, s,
+                       fused ? &wd : nullptr);
+    }
     return rc;
 }
 

@@ -152,8 +152,10 @@ struct DecodePlan {
 constexpr int kMaxDecodeRows = 65535;
 DecodePlan decode_plan(int n_rows, int n_q_heads, int n_kv_heads, int head_dim, int window,
                        int max_position);
+// fused: also write each row's token (rope, norm, K/V into its slot, q_out)
+// from the raw projection, in the workgroups that read the token's page
 hipError_t launch_decode(const AttnArgs& a, const DecodePlan& plan, void* workspace, hipStream_t s,
-                         Profiler* prof);
+                         Profiler* prof, const WriteArgs* fused = nullptr);
 
 // Prefill: tile list sizing and launch.
 size_t prefill_workspace(int n_tokens, int n_segments, int group, int head_dim);

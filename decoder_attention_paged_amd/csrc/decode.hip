@@ -19,7 +19,7 @@
 // Otherwise each chunk stores its fp32 (m, l, o) per head in the workspace
 // and a second, small kernel merges the chunks with the max-shifted rescale
 // (exactly the single-pass softmax in real arithmetic) and rounds to bf16.
-#include "dap_internal.h"
+#include "rope_head.h"
 
 namespace dap {
 
@@ -151,15 +151,24 @@ __device__ __forceinline__ void compute_unit(WaveState<D>& st, const UnitFrags<D
         st.o[db] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(as_bf16x8(f.v[db]), pf, st.o[db], 0, 0, 0);
 }
 
-template <int D>
+// kFused: the rows' tokens are also written here (step_paged's decode
+// tokens, one per row): every workgroup ropes (and norms) its g query heads
+// from the raw projection w.q into LDS, and the workgroup holding the row's
+// last page also writes the token's roped K, its V and q_out before any page
+// load, so its own key is in the pool when it is read. Other workgroups of
+// the row read only earlier pages.
+template <int D, bool kFused>
 __global__ __launch_bounds__(kDecodeThreads, 2) void decode_kernel(AttnArgs a, int pps, int max_splits,
-                                                                   float* __restrict__ ws) {
+                                                                   float* __restrict__ ws, WriteArgs w) {
     constexpr int kSteps = D / 32;     // QK k-steps of 32 dims
     constexpr int kDimBlocks = D / 16; // PV output blocks of 16 dims
 
     __shared__ float s_m[kDecodeWaves][16];
     __shared__ float s_l[kDecodeWaves][16];
     __shared__ int s_pg[kMaxPagesPerSplit];
+    __shared__ double s_cs[kFused ? D / 2 : 1], s_sn[kFused ? D / 2 : 1];
+    __shared__ __attribute__((aligned(16))) uint16_t s_q[kFused ? 16 * D : 8];
+    __shared__ long long s_slot;
     // per-wave O for the cross-wave merge, [wave][dim][head] for the g real
     // heads only (sized at launch: 4 * D * g floats)
     extern __shared__ float s_o[];
@@ -197,27 +206,6 @@ __global__ __launch_bounds__(kDecodeThreads, 2) void decode_kernel(AttnArgs a, i
         s_pg[i] = ok ? pg : -1;
     }
 
-    // q^T as the B operand: column = head, rows = dims 32s + 8*grp .. +7.
-    bf16x8 qf[kSteps];
-    {
-        const bool real = col < G;
-        const uint16_t* qrow = a.q + (long long)b * a.ld_q + (long long)(kh * G + (real ? col : 0)) * D;
-#pragma unroll
-        for (int s = 0; s < kSteps; ++s) {
-            u32x4 u = *reinterpret_cast<const u32x4*>(qrow + 32 * s + 8 * grp);
-            if (!real) u = u32x4{0u, 0u, 0u, 0u};
-            qf[s] = as_bf16x8(u);
-        }
-    }
-    __syncthreads();
-
-    const float c = kLog2e / sqrtf((float)D);
-    WaveState<D> st;
-    st.m = -INFINITY;
-    st.lsum = 0.f;
-#pragma unroll
-    for (int db = 0; db < kDimBlocks; ++db) st.o[db] = f32x4{0.f, 0.f, 0.f, 0.f};
-
     // units u = 2*page + half of this chunk; wave w takes u = w, w+4, ...
     // A unit is skipped if it lies past the chunk, its page id was bad, or
     // none of its keys is in [lo, p]. The next unit's fragments load while
@@ -240,11 +228,108 @@ __global__ __launch_bounds__(kDecodeThreads, 2) void decode_kernel(AttnArgs a, i
         return true;
     };
     UnitFrags<D> fa, fb;
-    int base_a = 0, base_b = 0, half;
-    const uint16_t *kt, *vt;
+    int base_a = 0, base_b = 0, half = 0;
+    const uint16_t *kt = a.k_pool, *vt = a.v_pool;
     int u = wave;
-    bool ok_a = prep(u, base_a, kt, vt, half);
-    load_unit<D>(fa, kt, vt, half, lane);
+    bool ok_a = false;
+    // The fused prologue issues the first unit's load before its rope work
+    // when that unit cannot hold the token's page (any workgroup but the
+    // writer, or a writer whose chunk has more than two pages).
+    const bool early_load = kFused && (split != 0 || n_local > 2);
+
+    if constexpr (kFused) {
+        // Waves 0-1 rope the g query heads (8 lanes a head) into LDS; in the
+        // workgroup holding the token's page (the chunk's last) also q_out,
+        // wave 2 the kv head's K and wave 3 its V, stored before the barrier
+        // below. The raw rows are loaded first, so their loads overlap the
+        // angle table; the token's slot is its page id, already in LDS.
+        const long long tok = (long long)b * w.ld_in;
+        const bool writer = split == 0;
+        const int j = wave < 2 ? tid % kLanesPerHead : lane;
+        const int hh = tid / kLanesPerHead;
+        const bool act = wave < 2 ? hh < G && j < D / 16 : (wave == 2 && writer && j < D / 16);
+        u32x4 lo = {0u, 0u, 0u, 0u}, hi = lo;
+        if (act) {
+            const uint16_t* src = wave < 2 ? w.q + tok + (long long)(kh * G + hh) * D : w.k + tok + (long long)kh * D;
+            lo = *reinterpret_cast<const u32x4*>(src + 8 * j);
+            hi = *reinterpret_cast<const u32x4*>(src + D / 2 + 8 * j);
+        }
+        constexpr int kVPerLane = (D + 63) / 64;
+        uint16_t vv[kVPerLane];
+        if (wave == 3 && writer)
+#pragma unroll
+            for (int i = 0; i < kVPerLane; ++i)
+                vv[i] = 64 * i + lane < D ? w.v[tok + (long long)kh * D + 64 * i + lane] : 0;
+        if (writer && tid == 0 && w.slots) s_slot = token_slot(w, b, rr.p, true);
+        angle_table<D>(w.inv_freq, rr.p, tid, kDecodeThreads, s_cs, s_sn);
+        __syncthreads();
+        if (early_load) {
+            ok_a = prep(u, base_a, kt, vt, half);
+            load_unit<D>(fa, kt, vt, half, lane);
+        }
+        long long slot = -1;
+        if (writer) {
+            if (w.slots) {
+                slot = s_slot;
+            } else {
+                const int pg = s_pg[n_local - 1];           // the page of position p (-1: flagged above)
+                slot = pg >= 0 ? (long long)pg * kPage + (rr.p & (kPage - 1)) : -1;
+            }
+        }
+        if (wave < 3) {
+            u32x4 ol, oh;
+            rope_chunk_pair<D>(w, wave < 2, j & 7, act, lo, hi, s_cs, s_sn, ol, oh);
+            if (act && wave < 2) {
+                *reinterpret_cast<u32x4*>(&s_q[hh * D + 8 * j]) = ol;
+                *reinterpret_cast<u32x4*>(&s_q[hh * D + D / 2 + 8 * j]) = oh;
+                if (writer) {
+                    uint16_t* dst = w.q_out + (long long)b * w.ld_q_out + (long long)(kh * G + hh) * D;
+                    *reinterpret_cast<u32x4*>(dst + 8 * j) = ol;
+                    *reinterpret_cast<u32x4*>(dst + D / 2 + 8 * j) = oh;
+                }
+            } else if (act && slot >= 0) {
+                const int in_page = (int)(slot & (kPage - 1));
+                uint16_t* tile = w.k_pool + ((slot >> 6) * w.n_kv_heads + kh) * (long long)(D * kPage);
+                *reinterpret_cast<u32x4*>(tile + k_tile_offset(in_page, 8 * j, D)) = ol;
+                *reinterpret_cast<u32x4*>(tile + k_tile_offset(in_page, D / 2 + 8 * j, D)) = oh;
+            }
+        } else if (writer && slot >= 0) {
+            const int in_page = (int)(slot & (kPage - 1));
+            uint16_t* tile = w.v_pool + ((slot >> 6) * w.n_kv_heads + kh) * (long long)(D * kPage);
+#pragma unroll
+            for (int i = 0; i < kVPerLane; ++i)
+                if (64 * i + lane < D) tile[v_tile_offset(in_page, 64 * i + lane, D)] = vv[i];
+        }
+        __syncthreads();        // the stores are complete before any page load below
+    }
+
+    // q^T as the B operand: column = head, rows = dims 32s + 8*grp .. +7.
+    bf16x8 qf[kSteps];
+    {
+        const bool real = col < G;
+        const uint16_t* qrow = kFused ? &s_q[(real ? col : 0) * D]
+                                      : a.q + (long long)b * a.ld_q + (long long)(kh * G + (real ? col : 0)) * D;
+#pragma unroll
+        for (int s = 0; s < kSteps; ++s) {
+            u32x4 u = *reinterpret_cast<const u32x4*>(qrow + 32 * s + 8 * grp);
+            if (!real) u = u32x4{0u, 0u, 0u, 0u};
+            qf[s] = as_bf16x8(u);
+        }
+    }
+    __syncthreads();
+
+    const float c = kLog2e / sqrtf((float)D);
+    WaveState<D> st;
+    st.m = -INFINITY;
+    st.lsum = 0.f;
+#pragma unroll
+    for (int db = 0; db < kDimBlocks; ++db) st.o[db] = f32x4{0.f, 0.f, 0.f, 0.f};
+
+    // (the first unit's load is issued above in the fused case when early)
+    if (!kFused || !early_load) {
+        ok_a = prep(u, base_a, kt, vt, half);
+        load_unit<D>(fa, kt, vt, half, lane);
+    }
     while (u < n_units) {
         const bool ok_b = prep(u + kDecodeWaves, base_b, kt, vt, half);
         load_unit<D>(fb, kt, vt, half, lane);
@@ -383,7 +468,7 @@ DecodePlan decode_plan(int n_rows, int n_q_heads, int n_kv_heads, int head_dim, 
 }
 
 hipError_t launch_decode(const AttnArgs& a, const DecodePlan& plan, void* workspace, hipStream_t s,
-                         Profiler* prof) {
+                         Profiler* prof, const WriteArgs* fused) {
     if (a.n_tokens <= 0) return hipSuccess;
     float* ws = static_cast<float*>(workspace);
     dim3 grid((unsigned)plan.max_splits * a.n_kv_heads * a.n_tokens), block(kDecodeThreads);
@@ -393,7 +478,10 @@ hipError_t launch_decode(const AttnArgs& a, const DecodePlan& plan, void* worksp
 #define DAP_DECODE_CASE(DD)                                                                             \
     case DD:                                                                                            \
         if (prof) prof->begin(DAP_KERNEL_DECODE, s);                                                    \
-        hipLaunchKernelGGL(decode_kernel<DD>, grid, block, lds, s, a, pps, ms, ws);                     \
+        if (fused)                                                                                      \
+            hipLaunchKernelGGL((decode_kernel<DD, true>), grid, block, lds, s, a, pps, ms, ws, *fused);   \
+        else                                                                                            \
+            hipLaunchKernelGGL((decode_kernel<DD, false>), grid, block, lds, s, a, pps, ms, ws, WriteArgs{}); \
         if (prof) prof->end(DAP_KERNEL_DECODE, s);                                                      \
         if (ms > 1) {                                                                                   \
             if (prof) prof->begin(DAP_KERNEL_DECODE_MERGE, s);                                          \

@@ -17,48 +17,15 @@
 // src/attention.linnet (q, k, v slices of the fused projection; rope of q
 // and k; write_tokens at each token's row and position); "Qwen3-4B"
 // (QK-norm per head slice, before rope, eps 1e-6).
-#include "dap_internal.h"
+#include "rope_head.h"
 
 namespace dap {
 
 namespace {
 
 constexpr int kWriteThreads = 256;
-constexpr int kLanesPerHead = 8;   // rotation work of one head: up to 8 lanes x 8 pairs
 
 constexpr int kVTile = 64;         // tokens per V-transpose workgroup
-
-// Slot of token t (-1 if an index is out of range; flags the error word).
-__device__ __forceinline__ long long token_slot(const WriteArgs& a, int t, int p, bool flag) {
-    if (p < 0 || p >= a.max_position) {
-        if (flag) atomicOr(a.err, kErrPosition);
-        return -1;
-    }
-    if (a.slots) {
-        const long long s = a.slots[t];
-        if (s < 0 || s >= (long long)a.n_pages * kPage) {
-            if (flag) atomicOr(a.err, kErrSlot);
-            return -1;
-        }
-        return s;
-    }
-    const int r = a.rows[t];
-    const int j = p / kPage;
-    if (r < 0 || r >= a.n_table_rows) {
-        if (flag) atomicOr(a.err, kErrRow);
-        return -1;
-    }
-    if (j >= a.table_ld) {
-        if (flag) atomicOr(a.err, kErrTable);
-        return -1;
-    }
-    const int pg = a.table[(long long)r * a.table_ld + j];
-    if (pg < 0 || pg >= a.n_pages) {
-        if (flag) atomicOr(a.err, kErrPage);
-        return -1;
-    }
-    return (long long)pg * kPage + (p % kPage);
-}
 
 // V of kVTile consecutive tokens, per kv head: rows read coalesced, turned
 // around in LDS, and stored along tokens. The tile layout keeps 8 consecutive
@@ -114,75 +81,6 @@ __device__ __forceinline__ void write_v_tile(const WriteArgs& a, int t0, int kh)
                      v_tile_offset((int)(slot & (kPage - 1)), d, D)] = s_v[at(d, tt)];
         }
     }
-}
-
-// One q or k head chunk pair of token t: lanes 8h..8h+7 of a head hold its
-// dims 8j..8j+7 and D/2+8j..D/2+8j+7 (rlo, rhi, raw bf16). Norm (the head's
-// sum of squares over its 8 lanes), rotate by the token's angles (cs, sn in
-// LDS), round once to bf16, store to q_out or the K tile. Every lane of the
-// wave calls it (the shuffles are wave-wide); inactive lanes store nothing.
-template <int D>
-__device__ __forceinline__ void rope_item(const WriteArgs& a, int t, int head, int j, bool active, u32x4 rlo,
-                                          u32x4 rhi, const double* cs, const double* sn, long long slot) {
-    constexpr int kHalf = D / 2;
-    const bool is_q = head < a.n_q_heads;
-    double xl[8], xh[8];
-#pragma unroll
-    for (int w = 0; w < 4; ++w) {
-        xl[2 * w] = (double)bf16_to_f32(rlo[w] & 0xffffu);
-        xl[2 * w + 1] = (double)bf16_to_f32(rlo[w] >> 16);
-        xh[2 * w] = (double)bf16_to_f32(rhi[w] & 0xffffu);
-        xh[2 * w + 1] = (double)bf16_to_f32(rhi[w] >> 16);
-    }
-    if (a.qk_norm) {
-        double ss = 0.0;
-#pragma unroll
-        for (int i = 0; i < 8; ++i) ss += xl[i] * xl[i] + xh[i] * xh[i];
-        ss += __shfl_xor(ss, 1);
-        ss += __shfl_xor(ss, 2);
-        ss += __shfl_xor(ss, 4);
-        if (active) {
-            const double denom = sqrt(ss / (double)D + a.eps);
-            const uint16_t* g = is_q ? a.q_gain : a.k_gain;
-            const u32x4 gl = *reinterpret_cast<const u32x4*>(g + 8 * j);
-            const u32x4 gh = *reinterpret_cast<const u32x4*>(g + kHalf + 8 * j);
-#pragma unroll
-            for (int w = 0; w < 4; ++w) {
-                xl[2 * w] = (double)bf16_to_f32(gl[w] & 0xffffu) * xl[2 * w] / denom;
-                xl[2 * w + 1] = (double)bf16_to_f32(gl[w] >> 16) * xl[2 * w + 1] / denom;
-                xh[2 * w] = (double)bf16_to_f32(gh[w] & 0xffffu) * xh[2 * w] / denom;
-                xh[2 * w + 1] = (double)bf16_to_f32(gh[w] >> 16) * xh[2 * w + 1] / denom;
-            }
-        }
-    }
-    if (!active) return;
-    u32x4 ol, oh;
-#pragma unroll
-    for (int w = 0; w < 4; ++w) {
-        uint32_t l2[2], h2[2];
-#pragma unroll
-        for (int e = 0; e < 2; ++e) {
-            const int i = 2 * w + e;
-            const double c = cs[8 * j + i];
-            const double s = sn[8 * j + i];
-            l2[e] = f64_to_bf16(xl[i] * c - xh[i] * s);
-            h2[e] = f64_to_bf16(xh[i] * c + xl[i] * s);
-        }
-        ol[w] = l2[0] | (l2[1] << 16);
-        oh[w] = h2[0] | (h2[1] << 16);
-    }
-    if (is_q) {
-        uint16_t* dst = a.q_out + (long long)t * a.ld_q_out + (long long)head * D;
-        *reinterpret_cast<u32x4*>(dst + 8 * j) = ol;
-        *reinterpret_cast<u32x4*>(dst + kHalf + 8 * j) = oh;
-        return;
-    }
-    if (slot < 0) return;
-    const int kh = head - a.n_q_heads;
-    const int in_page = (int)(slot & (kPage - 1));
-    uint16_t* tile = a.k_pool + ((slot >> 6) * a.n_kv_heads + kh) * (long long)(D * kPage);
-    *reinterpret_cast<u32x4*>(tile + k_tile_offset(in_page, 8 * j, D)) = ol;
-    *reinterpret_cast<u32x4*>(tile + k_tile_offset(in_page, kHalf + 8 * j, D)) = oh;
 }
 
 // raw rows of item `item` (8 lanes per head) of token t, zeros past the heads
@@ -241,13 +139,7 @@ __global__ __launch_bounds__(kWriteThreads) void rope_write_kernel(WriteArgs a) 
     long long slot = -1;
     if (have && lane == 0) slot = token_slot(a, t, p, true);
     slot = __shfl(slot, 0);
-    for (int i = lane; i < kHalf; i += 64) {
-        const double ang = (double)p * a.inv_freq[i];
-        double sn, cs;
-        sincos(ang, &sn, &cs);
-        s_sin[wave][i] = sn;
-        s_cos[wave][i] = cs;
-    }
+    angle_table<D>(a.inv_freq, p, lane, 64, s_cos[wave], s_sin[wave]);
     __syncthreads();
     if (!pos_ok) return;                             // uniform per wave; no barrier follows
 
@@ -297,13 +189,7 @@ __global__ __launch_bounds__(kWriteThreads) void rope_write_token_kernel(WriteAr
                          active[b]);
         if (it0 == 0) {                                       // uniform: the angle table, once
             if (tid == 0) s_slot = token_slot(a, t, p, true);
-            for (int i = tid; i < kHalf; i += kWriteThreads) {
-                const double ang = (double)p * a.inv_freq[i];
-                double sn, cs;
-                sincos(ang, &sn, &cs);
-                s_sin[i] = sn;
-                s_cos[i] = cs;
-            }
+            angle_table<D>(a.inv_freq, p, tid, kWriteThreads, s_cos, s_sin);
             __syncthreads();
             slot = s_slot;
         }

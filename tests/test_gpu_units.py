@@ -227,6 +227,69 @@ def test_step_paged_decode_sees_the_prompt_written_in_the_same_call():
     check_close(to_np_bits(out), ref, "step_paged over one call's own writes")
 
 
+@pytest.mark.parametrize("in_place", [False, True])
+@pytest.mark.parametrize("explicit_slots", [False, True])
+def test_step_paged_decode_only(in_place, explicit_slots):
+    """A decode step (no prompt tokens) with QK-norm: the decode writes each
+    row's token itself; with q_out over q (in place) every token is written
+    first instead. Either way q_out and K match the oracle bit for bit, V is
+    a bit copy, and the outputs match the oracle over the written pools."""
+    model = _model(8, 2, 128, 0, max_position=2048, theta=1e6, eps=1e-6)
+    wl = _workload(model, 6, 32, f"step-dec-{in_place}-{explicit_slots}")
+    kp, vp = device_pools(wl)
+    pos = np.array([5, 63, 64, 700, 1500, 2047], np.int32)
+    rows = np.arange(6, dtype=np.int32)
+    T = len(pos)
+    qkv = W.normal_matrix(wl.key("qkv"), T, model.qkv_width, "cuda")
+    D, hq, hkv = model.head_dim, model.n_q_heads, model.n_kv_heads
+    gains = (wl.gains("q", "cuda"), wl.gains("k", "cuda"))
+    slots = pages.slot_of(wl.table, rows, pos)
+    h = handle_for(model)
+    qkv_bits = to_np_bits(qkv)                 # before the call: in place, q is overwritten
+    q = qkv[:, :hq * D]
+    q_out, out = h.step_paged(q, qkv[:, hq * D:(hq + hkv) * D], qkv[:, (hq + hkv) * D:], torch_i32(pos),
+                              torch_i32(rows), torch_i32(wl.table), kp, vp, n_prompt=0, n_segments=1,
+                              slots=torch_i32(slots) if explicit_slots else None, q_gain=gains[0], k_gain=gains[1],
+                              q_out=q if in_place else None)
+    torch.cuda.synchronize()
+    g_np = (to_np_bits(gains[0]), to_np_bits(gains[1]))
+    _, q_bits, k_bits, v_bits = oracle_front(wl, qkv_bits, pos, g_np)
+    check_bits(to_np_bits(q_out).reshape(q_bits.shape), q_bits, "decode-step q_out")
+    kg, vg = dap.gather_slots(kp, vp, slots)
+    check_bits(to_np_bits(kg), k_bits, "decode-step K pages")
+    assert np.array_equal(to_np_bits(vg), v_bits), "decode-step V must be a bit copy"
+    op = OraclePool(wl, "cuda")
+    op.prefetch(wl.table.ravel())
+    op.write(slots, k_bits, v_bits)
+    ref = attention.paged(bf16.to_f64(q_bits), pos, rows, wl.table, op.read_page, 0)
+    check_close(to_np_bits(out), ref, "decode step over its own writes")
+
+
+def test_step_paged_validate_refuses_two_step_tokens_in_a_row():
+    """A decode-only call writes each row's token inside the decode, so it
+    takes one token per row: validate mode refuses two in one row. With
+    prompt tokens every token is written first, and a step token may even
+    precede its row's prompt tokens."""
+    model = _model(8, 2, 64, 0, max_position=1024)
+    wl = _workload(model, 3, 16, "step-validate")
+    kp, vp = device_pools(wl)
+    h = handle_for(model, validate=True)
+    D, hq, hkv = model.head_dim, model.n_q_heads, model.n_kv_heads
+
+    def call(pos, rows, n_prompt):
+        qkv = W.normal_matrix(wl.key("qkv"), len(pos), model.qkv_width, "cuda")
+        return h.step_paged(qkv[:, :hq * D], qkv[:, hq * D:(hq + hkv) * D], qkv[:, (hq + hkv) * D:],
+                            torch_i32(pos), torch_i32(rows), torch_i32(wl.table), kp, vp, n_prompt=n_prompt,
+                            n_segments=2)
+
+    call(np.array([10, 11], np.int32), np.array([1, 2], np.int32), 0)
+    call(np.array([10, 20, 30, 15], np.int32), np.array([0, 0, 0, 0], np.int32), 3)
+    with pytest.raises(dap.DapError) as e:
+        call(np.array([10, 11], np.int32), np.array([1, 1], np.int32), 0)
+    assert e.value.status == dap.BAD_INDEX
+    torch.cuda.synchronize()
+
+
 WRITE_MODELS = [
     _model(4, 2, 64, 0, 4096, theta=1e4),
     _model(32, 32, 96, 2047, 4096, theta=1e4),
