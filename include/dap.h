@@ -197,11 +197,11 @@ int dap_attn_decode_paged(dap_handle* handle,
  * Writes every token first, then runs the packed prefill on the prompt
  * tokens and the decode on the step tokens (q read from q_out), in that
  * order on `stream`; a token may attend slots any token of the call writes.
- * A call with no prompt tokens (a decode step) has no separate write: the
- * decode writes each row's token (q_out, K, V) itself, before it reads the
- * token's page. There each step token must have a row of its own (one
- * token per row; validate mode checks it) and q_out must not be q (with
- * q_out == q the call writes first, as above).
+ * A call with no prompt tokens (a decode step) over a small decode grid
+ * has no separate write: the decode writes each row's token (q_out, K, V)
+ * itself, before it reads the token's page. Each step token must then have
+ * a row of its own (one token per row; validate mode checks it), and q_out
+ * must not be q (with q_out == q the call writes first, as above).
  * out : [n_prompt + n_step][ld_out] bf16.
  * workspace : at least dap_step_workspace_bytes() bytes of scratch.
  */
