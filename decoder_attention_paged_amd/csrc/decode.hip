@@ -188,6 +188,28 @@ __global__ __launch_bounds__(kDecodeThreads, 2) void decode_kernel(AttnArgs a, i
     const int col = lane & 15;         // MFMA column: query head within the group
     const int grp = lane >> 4;         // lane group 0..3
 
+    // The decode-step form's inputs depend only on the row and kv head, so
+    // their loads are issued before the row's range and page ids are known.
+    const int G = a.n_q_heads / a.n_kv_heads;
+    const long long tok = kFused ? (long long)b * w.ld_in : 0;
+    const bool writer = split == 0;
+    const int j = wave < 2 ? tid % kLanesPerHead : lane;
+    const int hh = tid / kLanesPerHead;
+    const bool act = kFused && (wave < 2 ? hh < G && j < D / 16 : (wave == 2 && writer && j < D / 16));
+    u32x4 lo = {0u, 0u, 0u, 0u}, hi = lo;
+    if (act) {
+        const uint16_t* src = wave < 2 ? w.q + tok + (long long)(kh * G + hh) * D : w.k + tok + (long long)kh * D;
+        lo = *reinterpret_cast<const u32x4*>(src + 8 * j);
+        hi = *reinterpret_cast<const u32x4*>(src + D / 2 + 8 * j);
+    }
+    constexpr int kVPerLane = (D + 63) / 64;
+    uint16_t vv[kVPerLane];
+    if (kFused && wave == 3 && writer)
+#pragma unroll
+        for (int i = 0; i < kVPerLane; ++i)
+            vv[i] = 64 * i + lane < D ? w.v[tok + (long long)kh * D + 64 * i + lane] : 0;
+    const double freq = kFused && tid < D / 2 ? w.inv_freq[tid] : 0.0;
+
     const RowRange rr = row_range(a, b, split == 0 && kh == 0 && tid == 0);
     if (!rr.ok) return;
     const int n_splits = (rr.n_pg + pps - 1) / pps;
@@ -195,7 +217,6 @@ __global__ __launch_bounds__(kDecodeThreads, 2) void decode_kernel(AttnArgs a, i
     const int j_hi = rr.first_pg + rr.n_pg - 1 - split * pps;      // last page of this chunk
     const int j0 = max(rr.first_pg, j_hi - pps + 1);
     const int n_local = j_hi - j0 + 1;
-    const int G = a.n_q_heads / a.n_kv_heads;
 
     // this chunk's page ids, once, into LDS (-1 marks an out-of-range id)
     const int* trow = a.table + (long long)rr.row * a.table_ld;
@@ -241,27 +262,15 @@ __global__ __launch_bounds__(kDecodeThreads, 2) void decode_kernel(AttnArgs a, i
         // Waves 0-1 rope the g query heads (8 lanes a head) into LDS; in the
         // workgroup holding the token's page (the chunk's last) also q_out,
         // wave 2 the kv head's K and wave 3 its V, stored before the barrier
-        // below. The raw rows are loaded first, so their loads overlap the
-        // angle table; the token's slot is its page id, already in LDS.
-        const long long tok = (long long)b * w.ld_in;
-        const bool writer = split == 0;
-        const int j = wave < 2 ? tid % kLanesPerHead : lane;
-        const int hh = tid / kLanesPerHead;
-        const bool act = wave < 2 ? hh < G && j < D / 16 : (wave == 2 && writer && j < D / 16);
-        u32x4 lo = {0u, 0u, 0u, 0u}, hi = lo;
-        if (act) {
-            const uint16_t* src = wave < 2 ? w.q + tok + (long long)(kh * G + hh) * D : w.k + tok + (long long)kh * D;
-            lo = *reinterpret_cast<const u32x4*>(src + 8 * j);
-            hi = *reinterpret_cast<const u32x4*>(src + D / 2 + 8 * j);
-        }
-        constexpr int kVPerLane = (D + 63) / 64;
-        uint16_t vv[kVPerLane];
-        if (wave == 3 && writer)
-#pragma unroll
-            for (int i = 0; i < kVPerLane; ++i)
-                vv[i] = 64 * i + lane < D ? w.v[tok + (long long)kh * D + 64 * i + lane] : 0;
+        // below. The token's slot is its page id, already in LDS.
         if (writer && tid == 0 && w.slots) s_slot = token_slot(w, b, rr.p, true);
-        angle_table<D>(w.inv_freq, rr.p, tid, kDecodeThreads, s_cs, s_sn);
+        if (tid < D / 2) {
+            const double ang = (double)rr.p * freq;       // as the write kernel's angle table
+            double sn, cs;
+            sincos(ang, &sn, &cs);
+            s_sn[tid] = sn;
+            s_cs[tid] = cs;
+        }
         __syncthreads();
         if (early_load) {
             ok_a = prep(u, base_a, kt, vt, half);
