@@ -516,7 +516,10 @@ void prefill_kernel(AttnArgs a, const int* __restrict__ tiles, int cap) {
         for (int blk = 0; blk < 2; ++blk)
 #pragma unroll
             for (int r = 0; r < 16; ++r) mx = fmaxf(mx, sc[blk][r]);
-        mx = fmaxf(mx, __shfl_xor(mx, 32));
+        {   // the other half-wave's max, by a VALU lane swap (no LDS round trip)
+            const auto sw = __builtin_amdgcn_permlane32_swap(__float_as_uint(mx), __float_as_uint(mx), false, false);
+            mx = fmaxf(__uint_as_float(sw[0]), __uint_as_float(sw[1]));
+        }
         // Reference max in scaled log2 units: it moves to a row's new max only
         // when a score exceeds it by more than 2^kLazyMax (any visible key
         // sets an unset one), so the weights stay at most 2^kLazyMax and O and
