@@ -159,8 +159,11 @@ __global__ __launch_bounds__(kWriteThreads) void rope_write_kernel(WriteArgs a) 
 // workgroups per CU): 2176 tokens 34 -> 32 us against the 134 it would use.
 template <int D>
 __global__ __launch_bounds__(kWriteThreads, 4) void rope_write_token_kernel(WriteArgs a) {
-    if ((int)blockIdx.x >= a.n_tokens) {             // uniform per workgroup: V after the tokens
-        const int vb = (int)blockIdx.x - a.n_tokens;
+    const int n_vb = (a.n_tokens + kVTile - 1) / kVTile * a.n_kv_heads;
+    // V tiles first: dispatched last they ran as the kernel's tail (2176
+    // tokens of 8 kv heads: 32.0 -> 30.1 us)
+    if ((int)blockIdx.x < n_vb) {                    // uniform per workgroup
+        const int vb = (int)blockIdx.x;
         write_v_tile<D>(a, (vb / a.n_kv_heads) * kVTile, vb % a.n_kv_heads);
         return;
     }
@@ -171,7 +174,7 @@ __global__ __launch_bounds__(kWriteThreads, 4) void rope_write_token_kernel(Writ
     __shared__ long long s_slot;
 
     const int tid = threadIdx.x;
-    const int t = (int)blockIdx.x;
+    const int t = (int)blockIdx.x - n_vb;
     const int p = a.positions[t];
     if (p < 0 || p >= a.max_position) {                       // uniform per workgroup
         if (tid == 0) atomicOr(a.err, kErrPosition);
