@@ -65,6 +65,36 @@ def attend_one(q: np.ndarray, K: np.ndarray, V: np.ndarray, p: int, window: int)
     return out.reshape(hq, d)
 
 
+def attend_many(q: np.ndarray, K: np.ndarray, V: np.ndarray, positions, window: int) -> np.ndarray:
+    """Several query tokens of one row: q [n, Hq, D] at ``positions`` over the
+    row's keys/values [Hkv, > max(positions), D].
+
+    The same definition as attend_one for each query, written as one masked
+    product: the scores of every query against every key of the block's span
+    [min lo, max p], with keys outside a query's own range [lo, p] set to
+    -inf before its softmax, so their weight is exactly 0. Because a zero
+    weight still multiplies its key's value, every value in the span must be
+    finite (the row's written history, as it is for consecutive positions)."""
+    q = np.asarray(q, dtype=np.float64)
+    positions = np.asarray(positions, dtype=np.int64)
+    n, hq, d = q.shape
+    hkv = K.shape[0]
+    g = hq // hkv
+    lo = np.maximum(0, positions - window + 1) if window > 0 else np.zeros_like(positions)
+    a, b = int(lo.min()), int(positions.max()) + 1
+    Ks, Vs = K[:, a:b], V[:, a:b]                               # [Hkv, L, D]
+    qg = q.reshape(n, hkv, g, d).transpose(1, 0, 2, 3).reshape(hkv, n * g, d)
+    s = np.matmul(qg, np.swapaxes(Ks, -1, -2))                  # [Hkv, n*g, L]
+    s *= 1.0 / math.sqrt(d)
+    j = np.arange(a, b)
+    seen = (j[None, :] >= lo[:, None]) & (j[None, :] <= positions[:, None])   # [n, L]
+    np.copyto(s, -np.inf, where=~np.repeat(seen, g, axis=0)[None])
+    s -= np.max(s, axis=-1, keepdims=True)
+    e = np.exp(s, out=s)
+    out = np.matmul(e, Vs) / np.sum(e, axis=-1, keepdims=True)             # [Hkv, n*g, D]
+    return out.reshape(hkv, n, g, d).transpose(1, 0, 2, 3).reshape(n, hq, d)
+
+
 def paged(q: np.ndarray, positions, rows, table: np.ndarray, read_page, window: int = 0) -> np.ndarray:
     """Attention of query tokens over their rows' pages.
 

@@ -49,3 +49,26 @@ def from_f64(x) -> np.ndarray:
 def round_f64(x) -> np.ndarray:
     """Round float64 values to the nearest bf16 value, returned as float64."""
     return to_f64(from_f64(x))
+
+
+def near_tie(x, abs_tol: float = 1e-12) -> np.ndarray:
+    """Mask of float64 values within abs_tol of a bf16 rounding midpoint.
+
+    Such a value rounds one way or the other depending on its last few
+    float64 bits, so two correct float64 evaluations (different operation
+    orders, or sin/cos one ulp apart) may round it to adjacent bf16 values.
+    The midpoint on x's side of its nearest bf16 value v lies half a
+    spacing from v, the spacing being the gap from v to the next bf16
+    magnitude above (|x| > |v|) or below (|x| < |v|)."""
+    x = np.asarray(x, dtype=np.float64)
+    b = from_f64(x).astype(np.int64)
+    v = to_f64(b)
+    mag = b & 0x7FFF
+    sign = b & 0x8000
+    up = np.abs(to_f64(sign | np.minimum(mag + 1, 0x7F80)))
+    down = np.abs(to_f64(sign | np.maximum(mag - 1, 0)))
+    outward = np.abs(x) > np.abs(v)
+    gap = np.where(outward, up - np.abs(v), np.abs(v) - down)
+    with np.errstate(invalid="ignore"):
+        dist = 0.5 * gap - np.abs(x - v)
+        return np.isfinite(x) & (gap > 0) & (dist <= abs_tol)

@@ -10,9 +10,13 @@ pool. "Phi-3 Mini 4K Instruct" files, src/attention.linnet: the caches are
 Position j of table row r lives in physical page table[r][j // 64], at slot
 index j % 64 inside it; its pool slot number is page * 64 + j % 64.
 
-Pool layout (the library's documented contract, not the pages'), bf16:
+The oracle keeps its pools in a layout of its own (the pages fix only
+where a position lives, not how a page stores its elements), bf16:
   K pool [n_pages, n_kv_heads, 64, D]   one page tile per kv head, slot-major
   V pool [n_pages, n_kv_heads, D, 64]   one page tile per kv head, dim-major
+It is not the GPU library's tile layout: comparisons between the two go
+through logical [page, kv head, slot, dim] contents (page_logical here, the
+library's published per-element tile offsets on the other side).
 """
 import numpy as np
 
@@ -67,13 +71,13 @@ def page_logical(k_pool: np.ndarray, v_pool: np.ndarray, page: int, n_kv_heads: 
 
 
 def empty_pools(n_pages: int, n_kv_heads: int, head_dim: int, fill: int = 0):
-    """Flat-shaped K and V pools of bf16 bits in the library's layout."""
+    """Flat-shaped K and V pools of bf16 bits in the oracle's layout."""
     k = np.full((n_pages, n_kv_heads, PAGE, head_dim), fill, dtype=np.uint16)
     v = np.full((n_pages, n_kv_heads, head_dim, PAGE), fill, dtype=np.uint16)
     return k, v
 
 
 def pools_from_logical(k_logical: np.ndarray, v_logical: np.ndarray):
-    """Pools in the library's layout from logical [n_pages, Hkv, 64, D] contents."""
+    """Pools in the oracle's layout from logical [n_pages, Hkv, 64, D] contents."""
     return (np.ascontiguousarray(k_logical),
             np.ascontiguousarray(np.swapaxes(v_logical, -1, -2)))

@@ -279,3 +279,84 @@ def test_front_half_v_is_a_bit_copy_and_q_k_follow_norm_then_rope():
     qkv2[:, 2 * d: 3 * d] = bf16.from_f64(np.zeros((T, d)))      # zero q head 2
     q2, _, _ = core.prepare_tokens(qkv2, pos, hq, hkv, d, f)
     assert np.all(q2[:, 2] == 0) and np.array_equal(q2[:, [0, 1, 3]], q[:, [0, 1, 3]])
+
+
+def test_front_half_norm_then_rope_against_torch_and_transformers():
+    """prepare_tokens with distinct non-uniform q/k gains at positions > 0,
+    against an independent composition: torch's rms_norm on each head slice
+    ("Qwen3-4B", QK-norm paragraph: each head's slice, before rope), then
+    transformers' apply_rotary_pos_emb with cos/sin built from theta^(-2i/D).
+    Rope-before-norm and swapped gains are shown to disagree, so the check
+    can tell the compositions apart."""
+    import torch
+    from transformers.models.qwen3.modeling_qwen3 import apply_rotary_pos_emb
+
+    rng = np.random.default_rng(21)
+    hq, hkv, d, T, theta, eps = 8, 2, 128, 11, 1e6, 1e-6
+    qkv = bf16.from_f64(rng.standard_normal((T, (hq + 2 * hkv) * d)) * rng.uniform(0.1, 3.0, (T, 1)))
+    pos = rng.integers(1, 40000, T)
+    qg = bf16.from_f64(rng.uniform(0.5, 1.5, d))
+    kg = bf16.from_f64(rng.uniform(0.5, 1.5, d))
+    f = rope.inv_freq(theta, d)
+    q, k, _ = core.prepare_tokens(qkv, pos, hq, hkv, d, f, qg, kg, eps)
+
+    x = torch.from_numpy(bf16.to_f64(qkv))
+    tq = x[:, :hq * d].reshape(T, hq, d)
+    tk = x[:, hq * d:(hq + hkv) * d].reshape(T, hkv, d)
+    gq = torch.from_numpy(bf16.to_f64(qg))
+    gk = torch.from_numpy(bf16.to_f64(kg))
+    inv = 1.0 / theta ** (torch.arange(0, d, 2, dtype=torch.float64) / d)
+    ang = torch.from_numpy(pos.astype(np.float64))[:, None] * inv[None, :]
+    emb = torch.cat([ang, ang], dim=-1)                      # [T, D]
+    cos, sin = emb.cos(), emb.sin()
+
+    def compose(a, b, ga, gb, norm_first=True):
+        # transformers' layout: [batch, heads, seq, D] with cos/sin [batch, seq, D]
+        a4, b4 = a.permute(1, 0, 2)[None], b.permute(1, 0, 2)[None]
+        nrm = lambda t, g: torch.nn.functional.rms_norm(t, (d,), weight=g, eps=eps)
+        if norm_first:
+            a4, b4 = nrm(a4, ga), nrm(b4, gb)
+        ra, rb = apply_rotary_pos_emb(a4, b4, cos[None], sin[None])
+        if not norm_first:
+            ra, rb = nrm(ra, ga), nrm(rb, gb)
+        return ra[0].permute(1, 0, 2).numpy(), rb[0].permute(1, 0, 2).numpy()
+
+    ref_q, ref_k = compose(tq, tk, gq, gk)
+    # the two frequency formulas may differ in their last bit, which the
+    # angle (position up to 40000) scales to ~1e-11
+    assert np.allclose(q, ref_q, rtol=1e-9, atol=1e-9)
+    assert np.allclose(k, ref_k, rtol=1e-9, atol=1e-9)
+    # the plausible mistakes give clearly different values
+    wrong_order = compose(tq, tk, gq, gk, norm_first=False)
+    swapped = compose(tq, tk, gk, gq)
+    for wq, wk in (wrong_order, swapped):
+        assert np.max(np.abs(wq - q)) > 1e-2 and np.max(np.abs(wk - k)) > 1e-2
+
+
+@pytest.mark.parametrize("hq,hkv,d,window", [(4, 2, 64, 0), (8, 8, 96, 37), (32, 8, 128, 300), (16, 1, 64, 1)])
+def test_attend_many_matches_torch_sdpa_with_explicit_masks(hq, hkv, d, window):
+    """attend_many (a block of one row's queries in one masked product)
+    against torch's fp64 scaled_dot_product_attention given each query's
+    boolean mask over the row's keys, at unsorted, repeated and page-crossing
+    positions."""
+    import torch
+
+    rng = np.random.default_rng(hq * 1000 + d + window)
+    L = 700
+    K = rng.standard_normal((hkv, L, d))
+    V = rng.standard_normal((hkv, L, d))
+    pos = np.concatenate([rng.integers(0, L, 20), [0, 1, 63, 64, L - 1, L - 1]])
+    q = rng.standard_normal((len(pos), hq, d)) * 2.0
+    ours = attention.attend_many(q, K, V, pos, window)
+    g = hq // hkv
+    j = np.arange(L)
+    lo = np.maximum(0, pos - window + 1) if window > 0 else np.zeros_like(pos)
+    mask = torch.from_numpy((j[None, :] >= lo[:, None]) & (j[None, :] <= pos[:, None]))     # [n, L]
+    kt = torch.from_numpy(np.repeat(K, g, axis=0))                                           # [Hq, L, D]
+    vt = torch.from_numpy(np.repeat(V, g, axis=0))
+    qt = torch.from_numpy(q).transpose(0, 1)                                                 # [Hq, n, D]
+    ref = torch.nn.functional.scaled_dot_product_attention(qt, kt, vt, attn_mask=mask[None])
+    assert np.allclose(ours, ref.transpose(0, 1).numpy(), rtol=1e-12, atol=1e-13)
+    # and it agrees with the one-query form on every query
+    one = np.stack([attention.attend_one(q[i], K, V, int(pos[i]), window) for i in range(len(pos))])
+    assert np.allclose(ours, one, rtol=1e-12, atol=1e-13)

@@ -241,3 +241,24 @@ def test_qk_norm_is_per_head_not_flattened():
     flat = x.reshape(3, -1)
     yf = (flat / np.sqrt(np.mean(flat * flat, axis=-1, keepdims=True) + 1e-6)).reshape(x.shape)
     assert not np.allclose(yf, y, atol=1e-3)
+
+
+def test_near_tie_flags_exactly_the_rounding_midpoints():
+    # midpoints between adjacent bf16 values, built from their bit patterns
+    rng = np.random.default_rng(7)
+    bits = rng.integers(0x0001, 0x7F7F, 20000).astype(np.int64)
+    bits |= rng.integers(0, 2, bits.size) << 15            # both signs
+    lo = bf16.to_f64(bits)
+    hi = bf16.to_f64(bits + 1)                             # next magnitude, same sign
+    mid = 0.5 * (lo + hi)
+    assert bf16.near_tie(mid, 0.0).all()
+    # a quarter of the gap away from a midpoint is far from it
+    assert not bf16.near_tie(mid + 0.25 * (hi - lo), 0.0).any()
+    assert not bf16.near_tie(lo, 0.0).any()                # bf16 values themselves
+    # the spacing halves below a power of two: 1 - 2^-9 is a midpoint, 1 + 2^-9 is not
+    assert bf16.near_tie(np.array([1 - 2.0 ** -9, 1 + 2.0 ** -8, 2.0 ** -130 + 2.0 ** -134]), 0.0).all()
+    assert not bf16.near_tie(np.array([1 + 2.0 ** -9, 1 - 2.0 ** -10]), 0.0).any()
+    # the tolerance widens the band symmetrically
+    x = np.array([1 + 2.0 ** -8 + 5e-13, 1 + 2.0 ** -8 - 5e-13, 1 + 2.0 ** -8 + 2e-12])
+    assert list(bf16.near_tie(x, 1e-12)) == [True, True, False]
+    assert not bf16.near_tie(np.array([np.nan, np.inf, 0.0]), 1e-12).any()
