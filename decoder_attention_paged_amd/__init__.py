@@ -266,8 +266,8 @@ class Handle:
 
     @staticmethod
     def _workspace(ws, nbytes, like):
-        """A caller-kept workspace is reused as is (it must have been zeroed
-        once); otherwise a zeroed one is allocated for this call."""
+        """A caller-kept workspace is reused as is (its contents do not
+        matter); otherwise one is allocated for this call."""
         if ws is None:
             ws = torch.zeros(max(nbytes, 16), dtype=torch.uint8, device=like.device)
         _on_gpu("workspace", ws)
@@ -505,9 +505,11 @@ def tile_offsets(head_dim: int, device="cpu"):
 
 
 def pools(n_pages: int, n_kv_heads: int, head_dim: int, device="cuda", dtype=torch.bfloat16):
-    """Empty K and V pools: [n_pages, Hkv, 64 * D] each, one tile per (page,
-    kv head) in the library's tile layout. Use store_pages / pool_logical /
-    gather_slots to move logical [.., 64, D] contents in and out."""
+    """Uninitialised K and V pools: [n_pages, Hkv, 64 * D] each, one tile per
+    (page, kv head) in the library's tile layout. Slots no query attends may
+    hold anything (include/dap.h, stale slots). Use store_pages /
+    pool_logical / gather_slots to move logical [.., 64, D] contents in and
+    out."""
     k = torch.empty(n_pages, n_kv_heads, 64 * head_dim, dtype=dtype, device=device)
     v = torch.empty(n_pages, n_kv_heads, 64 * head_dim, dtype=dtype, device=device)
     return k, v

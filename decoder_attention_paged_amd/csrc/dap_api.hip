@@ -347,6 +347,7 @@ int do_decode(dap_handle* h, const uint16_t* q, int64_t ld_q, int32_t n_rows, co
     DAP_REQUIRE(!rows || aligned4(rows), DAP_INVALID_ARG, "rows must be aligned");
     const dap::DecodePlan plan = dap::decode_plan(n_rows, h->m.n_q_heads, h->m.n_kv_heads, h->m.head_dim,
                                                   h->m.window, h->m.max_position);
+    DAP_REQUIRE(dap::decode_plan_fits(plan), DAP_UNSUPPORTED, "decode split plan beyond the kernel's limits");
     DAP_REQUIRE(workspace && workspace_bytes >= plan.workspace_bytes && aligned16(workspace), DAP_WORKSPACE_TOO_SMALL,
                 "workspace must be 16-byte aligned and at least dap_decode_workspace_bytes()");
     DAP_REQUIRE((long long)plan.max_splits * h->m.n_kv_heads * n_rows < (1ll << 31), DAP_UNSUPPORTED,
@@ -642,7 +643,7 @@ int dap_create(const dap_model* mp, dap_handle** out) {
     DAP_REQUIRE(m.page_size == dap::kPage, DAP_UNSUPPORTED, "page_size must be 64");
     DAP_REQUIRE(m.window >= 0, DAP_INVALID_ARG, "window must be >= 0 (0 = none)");
     DAP_REQUIRE(m.max_position > 0, DAP_INVALID_ARG, "max_position must be positive");
-    DAP_REQUIRE(m.max_position <= (1 << 22), DAP_UNSUPPORTED, "max_position must be at most 4194304");
+    DAP_REQUIRE(m.max_position <= dap::kMaxPosition, DAP_UNSUPPORTED, "max_position must be at most 4194304");
     DAP_REQUIRE(m.rope_theta > 0 && std::isfinite(m.rope_theta), DAP_INVALID_ARG, "rope_theta must be positive");
     if (m.llama3) {
         DAP_REQUIRE(m.llama3_factor > 0 && m.llama3_low_freq_factor > 0 &&

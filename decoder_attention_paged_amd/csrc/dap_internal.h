@@ -7,10 +7,9 @@
 #include <stdint.h>
 
 #include "../../include/dap.h"
+#include "decode_plan.h"
 
 namespace dap {
-
-constexpr int kPage = 64;
 
 // Bits of the device error word (kernels OR them in when an index read from
 // device memory is out of range; the entry is skipped).
@@ -141,17 +140,7 @@ struct AttnArgs {
     unsigned* err;
 };
 
-// Decode: split count and workspace layout.
-// Workspace: partial o [n_rows][Hkv][max_splits][g][D] floats, then
-// (m, l) [n_rows][Hkv][max_splits][g][2] floats.
-struct DecodePlan {
-    int pages_per_split;
-    int max_splits;
-    size_t workspace_bytes;
-};
-constexpr int kMaxDecodeRows = 65535;
-DecodePlan decode_plan(int n_rows, int n_q_heads, int n_kv_heads, int head_dim, int window,
-                       int max_position);
+// Decode: split plan in decode_plan.h.
 // fused: also write each row's token (rope, norm, K/V into its slot, q_out)
 // from the raw projection, in the workgroups that read the token's page
 hipError_t launch_decode(const AttnArgs& a, const DecodePlan& plan, void* workspace, hipStream_t s,

@@ -25,11 +25,12 @@ namespace dap {
 
 namespace {
 
-constexpr int kDecodeThreads = 256;   // 4 waves
-constexpr int kDecodeWaves = 4;
+constexpr int kDecodeThreads = 64 * kDecodeWaves;
 constexpr float kLog2e = 1.4426950408889634f;
 
 __device__ __forceinline__ bf16x8 as_bf16x8(u32x4 u) { return __builtin_bit_cast(bf16x8, u); }
+typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
+constexpr bf16x2 kOnes2 = {(__bf16)1.0f, (__bf16)1.0f};
 
 // A wave works on 32-key units (half pages): two 16-key S blocks and the
 // V^T of the same 32 keys. The tile layout (dap_internal.h) stores each of
@@ -37,9 +38,6 @@ __device__ __forceinline__ bf16x8 as_bf16x8(u32x4 u) { return __builtin_bit_cast
 // by lane, with unit_key placing in lane group g's S values the 8 contiguous
 // keys its V fragment covers. The loads are non-temporal: the tiles are read
 // once per call, and contiguous kilobytes read that way stream fastest.
-
-constexpr int kMaxPagesPerSplit = 256;
-constexpr int kMaxSplits = 256;          // chunks per row (pps >= 4 caps this for max_position <= 65536)
 
 template <int D>
 struct UnitFrags {
@@ -102,8 +100,14 @@ struct WaveState {
 // One 32-key unit: S = K q^T, mask, online softmax, O^T += V^T P^T.
 // Running max m is kept in scaled log2 units (scale folded into one FMA);
 // O is rescaled only when some head's max moved in this unit.
+// On a unit that crosses lo or p, a key outside [lo, p] gets weight 0 and
+// its V elements are replaced by 0 before the PV product: such a slot may
+// hold anything a row left there earlier (NaN and Inf included), and 0 * NaN
+// would otherwise reach every head's sum. Lane group grp's V fragment holds
+// the same 8 keys (8 grp .. 8 grp + 7 of the unit) as its weights.
+// The normaliser adds the bf16 parts the PV product applies, two per dot2.
 template <int D>
-__device__ __forceinline__ void compute_unit(WaveState<D>& st, const UnitFrags<D>& f, const bf16x8* qf, float c,
+__device__ __forceinline__ void compute_unit(WaveState<D>& st, UnitFrags<D>& f, const bf16x8* qf, float c,
                                              int base, int lo, int p, int grp) {
     f32x4 sc[2];
 #pragma unroll
@@ -115,13 +119,26 @@ __device__ __forceinline__ void compute_unit(WaveState<D>& st, const UnitFrags<D
         sc[blk] = acc;
     }
     if (base < lo || base + 31 > p) {
+        // element e of the lane group's 8 keys is key base + 8 grp + e, in
+        // [lo, p] iff rl <= e <= rh (the empty asm keeps the compiler from
+        // turning each comparison into a loop-invariant register of its own);
+        // S block blk's value r is element 4 blk + r, V dword w holds 2w, 2w+1
+        int rl = lo - base - 8 * grp, rh = p - base - 8 * grp;
+        asm volatile("" : "+v"(rl), "+v"(rh));
+        bool in[8];
+#pragma unroll
+        for (int e = 0; e < 8; ++e) in[e] = e >= rl && e <= rh;
 #pragma unroll
         for (int blk = 0; blk < 2; ++blk)
 #pragma unroll
-            for (int r = 0; r < 4; ++r) {
-                const int kp = base + 8 * grp + 4 * blk + r;
-                if (kp < lo || kp > p) sc[blk][r] = -INFINITY;
-            }
+            for (int r = 0; r < 4; ++r)
+                if (!in[4 * blk + r]) sc[blk][r] = -INFINITY;
+        u32x4 keep;
+#pragma unroll
+        for (int w = 0; w < 4; ++w)
+            keep[w] = (in[2 * w] ? 0x0000ffffu : 0u) | (in[2 * w + 1] ? 0xffff0000u : 0u);
+#pragma unroll
+        for (int db = 0; db < D / 16; ++db) f.v[db] &= keep;
     }
     float mx = fmaxf(fmaxf(fmaxf(sc[0][0], sc[0][1]), fmaxf(sc[0][2], sc[0][3])),
                      fmaxf(fmaxf(sc[1][0], sc[1][1]), fmaxf(sc[1][2], sc[1][3])));
@@ -135,20 +152,37 @@ __device__ __forceinline__ void compute_unit(WaveState<D>& st, const UnitFrags<D
         for (int db = 0; db < D / 16; ++db) st.o[db] *= alpha;
         st.m = m_new;
     }
-    float ps = 0.f;
-    bf16x8 pf;
+    // Each weight w goes to the PV product as two bf16 parts, hi = bf16(w)
+    // and lo = bf16(w - hi), so the weights applied carry 16 significant
+    // bits: the rounding no longer depends on the running max the chunk has
+    // reached, and the result does not depend on how the row is split into
+    // chunks beyond float32 rounding. (The decode is bound by its page
+    // reads; the second set of PV MFMAs is nearly free.)
+    bf16x8 pf, pl;
 #pragma unroll
     for (int blk = 0; blk < 2; ++blk)
 #pragma unroll
         for (int r = 0; r < 4; ++r) {
-            const float e = __builtin_amdgcn_exp2f(__builtin_fmaf(sc[blk][r], c, -st.m));
-            ps += e;
-            pf[4 * blk + r] = (__bf16)e;
+            const float w = __builtin_amdgcn_exp2f(__builtin_fmaf(sc[blk][r], c, -st.m));
+            const __bf16 hi = (__bf16)w;
+            pf[4 * blk + r] = hi;
+            pl[4 * blk + r] = (__bf16)(w - (float)hi);
         }
-    st.lsum += ps;
+    float ps0 = __builtin_amdgcn_fdot2_f32_bf16(__builtin_shufflevector(pf, pf, 0, 1), kOnes2, 0.f, false);
+    float ps1 = __builtin_amdgcn_fdot2_f32_bf16(__builtin_shufflevector(pf, pf, 2, 3), kOnes2, 0.f, false);
+    ps0 = __builtin_amdgcn_fdot2_f32_bf16(__builtin_shufflevector(pf, pf, 4, 5), kOnes2, ps0, false);
+    ps1 = __builtin_amdgcn_fdot2_f32_bf16(__builtin_shufflevector(pf, pf, 6, 7), kOnes2, ps1, false);
+    ps0 = __builtin_amdgcn_fdot2_f32_bf16(__builtin_shufflevector(pl, pl, 0, 1), kOnes2, ps0, false);
+    ps1 = __builtin_amdgcn_fdot2_f32_bf16(__builtin_shufflevector(pl, pl, 2, 3), kOnes2, ps1, false);
+    ps0 = __builtin_amdgcn_fdot2_f32_bf16(__builtin_shufflevector(pl, pl, 4, 5), kOnes2, ps0, false);
+    ps1 = __builtin_amdgcn_fdot2_f32_bf16(__builtin_shufflevector(pl, pl, 6, 7), kOnes2, ps1, false);
+    st.lsum += ps0 + ps1;
 #pragma unroll
     for (int db = 0; db < D / 16; ++db)
         st.o[db] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(as_bf16x8(f.v[db]), pf, st.o[db], 0, 0, 0);
+#pragma unroll
+    for (int db = 0; db < D / 16; ++db)
+        st.o[db] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(as_bf16x8(f.v[db]), pl, st.o[db], 0, 0, 0);
 }
 
 // kFused: the rows' tokens are also written here (step_paged's decode
@@ -455,26 +489,6 @@ __global__ __launch_bounds__(kDecodeThreads) void decode_merge_kernel(AttnArgs a
 }
 
 }  // namespace
-
-DecodePlan decode_plan(int n_rows, int n_q_heads, int n_kv_heads, int head_dim, int window,
-                       int max_position) {
-    DecodePlan p;
-    const int span = window > 0 ? min(window, max_position) : max_position;
-    const int max_pages = (span + kPage - 1) / kPage + (window > 0 ? 1 : 0);
-    const long long pairs = (long long)n_rows * n_kv_heads;
-    // aim at ~8K workgroups in total (about half active for uniformly spread
-    // lengths), at least one page per wave
-    long long pps = (pairs * max_pages + 8191) / 8192;
-    pps = (pps + kDecodeWaves - 1) / kDecodeWaves * kDecodeWaves;
-    if (pps < kDecodeWaves) pps = kDecodeWaves;
-    if (pps > kMaxPagesPerSplit) pps = kMaxPagesPerSplit;
-    if ((max_pages + pps - 1) / pps > kMaxSplits) pps = (max_pages + kMaxSplits - 1) / kMaxSplits;
-    p.pages_per_split = (int)pps;
-    p.max_splits = (int)((max_pages + pps - 1) / pps);
-    // partials: o [n_rows][Hkv][max_splits][g][D], then (m, l) [n_rows][Hkv][max_splits][g][2]
-    p.workspace_bytes = (size_t)n_rows * n_q_heads * p.max_splits * (head_dim + 2) * sizeof(float);
-    return p;
-}
 
 hipError_t launch_decode(const AttnArgs& a, const DecodePlan& plan, void* workspace, hipStream_t s,
                          Profiler* prof, const WriteArgs* fused) {

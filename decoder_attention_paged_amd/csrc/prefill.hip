@@ -511,6 +511,29 @@ void prefill_kernel(AttnArgs a, const int* __restrict__ tiles, int cap) {
                     if (kp < lo || kp > p) sc[blk][r] = -INFINITY;
                 }
         }
+        // Keys no row of this wave attends (outside [w_lomin, w_pmax]) may
+        // hold anything an earlier request left (NaN and Inf included):
+        // their V elements become 0, so their zero weights add exactly 0.
+        // Lane (row, half) holds in V^T fragment t the keys 16 t + 8 half
+        // .. + 7, two per dword.
+        if (k0 < w_lomin || k0 + kPage - 1 > w_pmax) {
+            // element e of fragment t is kept iff rl <= 16 t + e <= rh (the
+            // empty asm keeps the comparisons from becoming loop invariants)
+            int rl = w_lomin - k0 - 8 * half, rh = w_pmax - k0 - 8 * half;
+            asm volatile("" : "+v"(rl), "+v"(rh));
+#pragma unroll
+            for (int t = 0; t < 4; ++t) {
+                u32x4 keep;
+#pragma unroll
+                for (int w = 0; w < 4; ++w) {
+                    const int e = 16 * t + 2 * w;
+                    keep[w] = (e >= rl && e <= rh ? 0x0000ffffu : 0u) |
+                              (e + 1 >= rl && e + 1 <= rh ? 0xffff0000u : 0u);
+                }
+#pragma unroll
+                for (int db = 0; db < kDimBlocks; ++db) vfr[t][db] &= keep;
+            }
+        }
         float mx = -INFINITY;
 #pragma unroll
         for (int blk = 0; blk < 2; ++blk)

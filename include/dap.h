@@ -38,6 +38,21 @@
  * j%64; its slot number is page*64 + j%64. (The pages: "Mistral 7B Instruct
  * v0.3", Entries table, decode_paged: a pool of positions in pages of
  * PageSize 64, row b's positions in the pages table[b] lists.)
+ *
+ * Stale slots. A slot that no query of a call attends may hold any bits,
+ * NaN and Inf included (what an earlier request left there, or memory never
+ * written): it changes no output. ("Phi-3 Mini 4K Instruct" files,
+ * src/attention.linnet, prefill_slots: the rest of a row keeps what an
+ * earlier request left, since decoding never reads past its own position.)
+ * The kernels load whole pages, give such keys weight 0 and set their V
+ * elements to 0 before the weighted sum. One qualification: the packed
+ * prefill takes the tokens of a run of equal segment ids 32 at a time and
+ * clears V only outside such a group's span (its lowest window start to its
+ * highest position), so every slot inside the span must hold a finite
+ * value. With consecutive positions in each run (prompts and chunks packed
+ * end to end) every slot of the span is attended by some token of the
+ * group, i.e. it is written history. Pools therefore need no initial
+ * state, and the workspaces below may hold anything on entry.
  */
 #ifndef DAP_H
 #define DAP_H

@@ -25,3 +25,17 @@ def pytest_collection_modifyitems(config, items):
     for item in items:
         if "gpu" in item.keywords:
             item.add_marker(skip)
+
+
+def pytest_terminal_summary(terminalreporter):
+    """Bit-exactness report: elements the oracle flagged as near a bf16
+    rounding midpoint, and how many of them the GPU rounded the other way."""
+    parity = sys.modules.get("parity")
+    rep = getattr(parity, "TIE_REPORT", None)
+    if not rep:
+        return
+    n = sum(r[1] for r in rep)
+    flagged = sum(r[2] for r in rep)
+    diff = sum(r[3] for r in rep)
+    terminalreporter.write_line(f"bit-exact checks: {len(rep)} calls, {n} rounded elements, {flagged} flagged "
+                                f"near-ties, {diff} differing (all of them flagged)")

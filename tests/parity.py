@@ -19,6 +19,8 @@ from oracle import attention, bf16, core, pages, rope
 ATOL = 2e-2
 RTOL = 2e-2
 REL_RMS = 1e-2
+TIE_TOL = 1e-12
+TIE_REPORT = []        # (what, elements, flagged near-ties, differing) per check_bits call
 
 
 def handle_for(model: W.ModelShape, validate=False) -> dap.Handle:
@@ -95,13 +97,30 @@ def row_pages(wl: W.Workload, rows, positions):
     return sorted(ids)
 
 
+class RoundedBits(np.ndarray):
+    """bf16 bit patterns the oracle rounded from float64, carrying ``tie``: the
+    mask of elements whose float64 value lies within 1e-12 of a bf16 rounding
+    midpoint (bf16.near_tie). Only the array oracle_front returns carries it;
+    slices, reshapes and arithmetic give plain strict arrays (tie None)."""
+
+    def __array_finalize__(self, obj):
+        self.tie = None
+
+
+def _rounded(x):
+    r = bf16.from_f64(x).view(RoundedBits)
+    r.tie = bf16.near_tie(x, TIE_TOL)
+    return r
+
+
 def oracle_front(wl: W.Workload, qkv_bits: np.ndarray, positions, gains=None):
-    """Oracle q (float64), rounded q and k bits, and v bits for tokens."""
+    """Oracle q (float64), rounded q and k bits (RoundedBits, with their
+    near-tie masks), and v bits for tokens."""
     m = wl.model
     qg, kg = (gains if gains is not None else (None, None))
     q, k, vb = core.prepare_tokens(qkv_bits, positions, m.n_q_heads, m.n_kv_heads, m.head_dim,
                                    oracle_freqs(m), qg, kg, m.qk_norm_eps)
-    return q, bf16.from_f64(q), bf16.from_f64(k), vb
+    return q, _rounded(q), _rounded(k), vb
 
 
 def check_close(gpu_bits: np.ndarray, ref: np.ndarray, what: str):
@@ -120,22 +139,61 @@ def check_close(gpu_bits: np.ndarray, ref: np.ndarray, what: str):
     return msg
 
 
-def check_bits(gpu_bits: np.ndarray, ref_bits: np.ndarray, what: str, min_identical=0.9999):
-    """Rounded values: >= 99.99% bit-identical and every one within 1 bf16 ulp."""
-    a = gpu_bits.astype(np.int64).reshape(-1)
-    b = ref_bits.astype(np.int64).reshape(-1)
+def check_bits(gpu_bits: np.ndarray, ref_bits: np.ndarray, what: str):
+    """Rounded values must equal the oracle's rounding bit for bit. The only
+    exception is an element the oracle flagged as lying within 1e-12 of a
+    bf16 rounding midpoint (``ref_bits.tie``), where two correct float64
+    evaluations may round to adjacent values: it may differ by one ulp. The
+    number flagged is recorded in TIE_REPORT and printed at the session's end."""
+    a = np.asarray(gpu_bits).astype(np.int64).reshape(-1)
+    b = np.asarray(ref_bits).astype(np.int64).reshape(-1)
+    assert a.shape == b.shape, f"{what}: {a.shape} values against {b.shape}"
+    tie = getattr(ref_bits, "tie", None)
+    tie = np.zeros(a.shape, bool) if tie is None else np.asarray(tie).reshape(-1)
     same = a == b
+    off = ~same & ~tie
+    assert not off.any(), (f"{what}: {int(off.sum())} of {a.size} values differ from the oracle's rounding "
+                           f"(first at {int(np.nonzero(off)[0][0])}: {a[off][0]:#06x} vs {b[off][0]:#06x})")
     # adjacent bf16 values of the same sign differ by 1 in the bit pattern
-    ulp = np.abs(a - b)
-    frac = same.mean() if same.size else 1.0
-    assert frac >= min_identical, f"{what}: only {frac:.6f} of values bit-identical"
-    assert np.all(same | ((ulp == 1) & ((a ^ b) & 0x8000 == 0))), f"{what}: a value differs by more than 1 ulp"
-    return frac
+    near = (np.abs(a - b) == 1) & ((a ^ b) & 0x8000 == 0)
+    assert np.all(same | near), f"{what}: a flagged near-tie value differs by more than 1 ulp"
+    TIE_REPORT.append((what, a.size, int(tie.sum()), int((~same).sum())))
+    return int(tie.sum())
 
 
 def oracle_attention(wl, opool: OraclePool, q_f64, positions, rows):
     opool.prefetch(row_pages(wl, rows, positions))
     return attention.paged(q_f64, positions, rows, wl.table, opool.read_page, wl.model.window)
+
+
+def oracle_rows(wl: W.Workload, opool: OraclePool, qs, positions, rows, block=32):
+    """Oracle attention for one or more query sets (e.g. q and the peaky 4q)
+    at the same (row, position) pairs, row by row: each row's pages are
+    regenerated (with the oracle's own writes in ``opool``) once for all the
+    query sets and dropped before the next row, and its queries run in
+    position-sorted blocks of ``block`` tokens through attention.attend_many.
+    Memory stays bounded by one row, so every row of the largest pools can be
+    checked. Returns a list of outputs, one per query set."""
+    qs = [np.asarray(q, dtype=np.float64) for q in qs]
+    positions = np.asarray(positions, dtype=np.int64)
+    rows = np.asarray(rows, dtype=np.int64)
+    outs = [np.empty_like(q) for q in qs]
+    win = wl.model.window
+    for r in np.unique(rows):
+        idx = np.nonzero(rows == r)[0]
+        idx = idx[np.argsort(positions[idx], kind="stable")]
+        n = int(positions[idx].max()) + 1
+        tmp = OraclePool(wl, opool.gen_device)
+        tmp.overlay = opool.overlay
+        tmp.prefetch(wl.table[r, :-(-n // 64)])
+        K, V = attention.gather_row(wl.table[r], n, tmp.read_page)
+        del tmp
+        for s0 in range(0, len(idx), block):
+            b = idx[s0:s0 + block]
+            for q, out in zip(qs, outs):
+                out[b] = attention.attend_many(q[b], K, V, positions[b], win)
+        del K, V
+    return outs
 
 
 def torch_i32(a, device="cuda"):

@@ -63,26 +63,59 @@ def test_decode_matches_oracle(hq, hkv, d, window, peaky):
     check_close(to_np_bits(out), ref, f"decode {hq}/{hkv}/{d} w{window}")
 
 
-def test_decode_rows_indirection_and_split_invariance():
-    model = _model(32, 8, 128, 0, max_position=4096)
+def _bf16_ulp(x):
+    """Spacing of bf16 values at |x| (2^(e-7) for |x| in [2^e, 2^(e+1)))."""
+    x = np.maximum(np.abs(x), 2.0 ** -126)
+    return np.ldexp(1.0, np.floor(np.log2(x)).astype(int) - 7)
+
+
+@pytest.mark.parametrize("peaky", [False, True])
+def test_decode_rows_indirection_and_split_invariance(peaky):
+    """The same rows decoded with one chunk per row, two, eight and sixteen
+    (the chunk size follows the call's size, so the rows are repeated 16, 8,
+    2 and 1 times), and under other handles' chunkings. The merge is exact in
+    real arithmetic and the decode applies each weight with 16 significant
+    bits (a bf16 pair), so every chunking must agree with the one-chunk
+    result to float32 rounding, and every result must lie within one bf16
+    ulp (plus 2^-20 for float32 cancellation) of the fp64 oracle."""
+    model = _model(32, 8, 128, 0, max_position=65536)
     wl = _workload(model, 8, 64, "dec-rows")
     kp, vp = device_pools(wl)
     rows = np.array([7, 2, 2, 5], np.int32)
     positions = np.array([4095, 4000, 130, 64], np.int32)
-    q = _queries(wl, 4)
-    outs = []
-    for max_pos in (4096, 65536, 1 << 20):           # different page chunking
-        m2 = _model(32, 8, 128, 0, max_position=max_pos)
-        h = handle_for(m2)
-        outs.append(h.attn_decode_paged(q, torch_i32(positions), torch_i32(wl.table), kp, vp,
-                                        rows=torch_i32(rows)).view(torch.bfloat16).float())
+    q = _queries(wl, 4, 4.0 if peaky else 1.0)
+    h = handle_for(model)
+    results = {}
+    for rep in (16, 8, 2, 1):           # 1, 2, 8 and 16 chunks for the 64-page row
+        n = 4 * rep
+        # the chunk size, from the library's workspace query: n rows x Hq x
+        # chunks per row (for the longest row, 1024 pages) x (D + 2) floats
+        splits = h.decode_workspace_bytes(n) // (n * 32 * 130 * 4)
+        chunks = -(-64 // (1024 // splits))
+        out = h.attn_decode_paged(q.repeat(rep, 1), torch_i32(np.tile(positions, rep)), torch_i32(wl.table), kp, vp,
+                                  rows=torch_i32(np.tile(rows, rep)))
+        o = to_np_bits(out).reshape(rep, 4, -1)
+        assert all(np.array_equal(o[0], o[i]) for i in range(rep)), "repeated rows differ within one call"
+        results[chunks] = o[0]
+    assert sorted(results) == [1, 2, 8, 16], sorted(results)
+    for max_pos in (4096, 1 << 20):                  # other handles, other chunkings
+        h2 = handle_for(_model(32, 8, 128, 0, max_position=max_pos))
+        out = h2.attn_decode_paged(q, torch_i32(positions), torch_i32(wl.table), kp, vp, rows=torch_i32(rows))
+        results[f"max_position {max_pos}"] = to_np_bits(out)
     torch.cuda.synchronize()
     op = OraclePool(wl, "cuda")
     ref = attention.paged(bf16.to_f64(to_np_bits(q)).reshape(4, 32, 128), positions, rows, wl.table,
-                          op.read_page, 0)
-    check_close(to_np_bits(outs[0].to(torch.bfloat16)), ref, "decode rows")
-    for o in outs[1:]:
-        assert torch.allclose(o, outs[0], atol=1e-2, rtol=0)
+                          op.read_page, 0).reshape(4, -1)
+    check_close(results[1], ref, "decode rows, one chunk")
+    one = bf16.to_f64(results[1])
+    for k, bits in results.items():
+        o = bf16.to_f64(bits)
+        diff = np.abs(o - one)
+        assert np.all(diff <= _bf16_ulp(np.maximum(np.abs(o), np.abs(one))) + 2.0 ** -20), \
+            f"{k} chunks: max difference {diff.max():.3e} from the one-chunk result"
+        err = np.abs(o - ref)
+        assert np.all(err <= _bf16_ulp(ref) + 2.0 ** -20), \
+            f"{k} chunks: max error {err.max():.3e} from the oracle, beyond one bf16 ulp"
 
 
 PREFILL_SHAPES = [(4, 2, 64, 0), (32, 32, 96, 2047), (32, 8, 128, 0), (8, 8, 128, 40), (8, 2, 96, 0)]
