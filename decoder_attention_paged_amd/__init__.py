@@ -25,7 +25,8 @@ OK, INVALID_ARG, UNSUPPORTED, WORKSPACE_TOO_SMALL, HIP_ERROR, BAD_INDEX = 0, -1,
 
 EXPORTS = ("dap_create", "dap_destroy", "dap_last_error", "dap_set_validate", "dap_inv_freq",
            "dap_rope_qknorm_write_pages", "dap_prefill_workspace_bytes", "dap_attn_prefill_packed",
-           "dap_decode_workspace_bytes", "dap_attn_decode_paged", "dap_step_workspace_bytes",
+           "dap_decode_workspace_bytes", "dap_attn_decode_paged", "dap_attn_decode_paged_noalloc",
+           "dap_step_workspace_bytes",
            "dap_step_paged", "dap_set_profiling", "dap_profile_read", "dap_cache_workspace_bytes",
            "dap_decode", "dap_decode_rows", "dap_prefill", "dap_prefill_slots", "dap_inpass_workspace_bytes",
            "dap_packed", "dap_forward", "dap_tile_layout")
@@ -85,6 +86,8 @@ def load_library(path: str = LIB_PATH):
     lib.dap_decode_workspace_bytes.restype = _SZ
     lib.dap_attn_decode_paged.argtypes = [
         _P, _P, _I64, _I32, _P, _P, _P, _I32, _I32, _P, _P, _I32, _P, _I64, _P, _SZ, _P]
+    lib.dap_attn_decode_paged_noalloc.argtypes = [
+        _P, _P, _I64, _I32, _P, _P, _P, _I32, _I32, _P, _P, _I32, _P, _I64, _P]
     lib.dap_step_workspace_bytes.argtypes = [_P, _I32, _I32, _I32]
     lib.dap_step_workspace_bytes.restype = _SZ
     lib.dap_step_paged.argtypes = [
@@ -330,6 +333,17 @@ class Handle:
             self._h, _ptr(_bf16(q)), _ld(q), R, _ptr(_i32(positions)), _ptr(_i32(rows)),
             _ptr(_i32(table)), table.shape[1], table.shape[0], _ptr(_bf16(k_pool)), _ptr(_bf16(v_pool)),
             k_pool.shape[0], _ptr(_bf16(out)), _ld(out), _ptr(ws), ws.numel(), _stream(stream)))
+        return out
+
+    def attn_decode_paged_noalloc(self, q, positions, table, k_pool, v_pool, *, out, rows=None, stream=None):
+        """attn_decode_paged with no workspace: the library's static device
+        scratch holds the partials. ``out`` is required (nothing is allocated)."""
+        R = positions.shape[0]
+        self._check_attn(R, q, positions, rows, out, k_pool, v_pool, table)
+        _check(_lib.dap_attn_decode_paged_noalloc(
+            self._h, _ptr(_bf16(q)), _ld(q), R, _ptr(_i32(positions)), _ptr(_i32(rows)),
+            _ptr(_i32(table)), table.shape[1], table.shape[0], _ptr(_bf16(k_pool)), _ptr(_bf16(v_pool)),
+            k_pool.shape[0], _ptr(_bf16(out)), _ld(out), _stream(stream)))
         return out
 
     def step_paged(self, q, k, v, positions, rows, table, k_pool, v_pool, *, n_prompt, n_segments,

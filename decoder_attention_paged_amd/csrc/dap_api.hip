@@ -2,6 +2,7 @@
 #include <cmath>
 #include <cstdio>
 #include <cstring>
+#include <mutex>
 #include <string>
 #include <algorithm>
 #include <unordered_set>
@@ -66,9 +67,41 @@ void Profiler::end(int, hipStream_t s) {
 
 }  // namespace dap
 
+// ---------------------------------------------------------------- static decode scratch
+// dap_attn_decode_paged_noalloc keeps the decode's per-chunk partials in this
+// file-scope device array instead of a caller workspace. Every device the
+// library runs on holds its own copy until the process ends, and every call
+// on that device shares it (overlapping calls on one device race). In host
+// code the name is only a stand-in for the symbol, not a device address:
+// the address comes from hipGetSymbolAddress, once per device (at the first
+// dap_create there, with that device current), and is what the kernels get.
+namespace {
+constexpr size_t kScratchBytes = size_t(32) << 20;
+constexpr int kScratchDevices = 64;
+std::mutex g_scratch_mu;
+void* g_scratch_ptr[kScratchDevices] = {};
+}  // namespace
+static __device__ __align__(256) unsigned char scratch[kScratchBytes];
+
+static hipError_t scratch_address(int dev, void** out) {
+    *out = nullptr;
+    if (dev < 0 || dev >= kScratchDevices) return hipErrorInvalidDevice;
+    std::lock_guard<std::mutex> lock(g_scratch_mu);
+    if (!g_scratch_ptr[dev]) {
+        void* p = nullptr;
+        const hipError_t e = hipGetSymbolAddress(&p, HIP_SYMBOL(scratch));
+        if (e != hipSuccess) return e;
+        if (!p) return hipErrorInvalidSymbol;
+        g_scratch_ptr[dev] = p;
+    }
+    *out = g_scratch_ptr[dev];
+    return hipSuccess;
+}
+
 struct dap_handle {
     dap_model m;
     int device;
+    void* scratch;     // this device's static decode scratch (its device address)
     int group;
     std::vector<double> h_inv_freq;
     double* d_inv_freq;
@@ -662,7 +695,9 @@ int dap_create(const dap_model* mp, dap_handle** out) {
     h->prof_state = nullptr;
     h->prof.st = nullptr;
     h->h_inv_freq = build_inv_freq(m);
+    h->scratch = nullptr;
     hipError_t e = hipGetDevice(&h->device);
+    if (e == hipSuccess) e = scratch_address(h->device, &h->scratch);
     if (e == hipSuccess) e = hipMalloc(&h->d_inv_freq, h->h_inv_freq.size() * sizeof(double));
     if (e == hipSuccess) e = hipMalloc(&h->d_err, 256);
     if (e == hipSuccess)
@@ -775,6 +810,29 @@ int dap_attn_decode_paged(dap_handle* h, const uint16_t* q, int64_t ld_q, int32_
     if (int rc = check_handle(h)) return rc;
     return do_decode(h, q, ld_q, n_rows, positions, rows, table, table_ld, n_table_rows, k_pool, v_pool, n_pages, out,
                      ld_out, workspace, workspace_bytes, static_cast<hipStream_t>(stream));
+}
+
+int dap_attn_decode_paged_noalloc(dap_handle* h, const uint16_t* q, int64_t ld_q, int32_t n_rows,
+                                  const int32_t* positions, const int32_t* rows, const int32_t* table,
+                                  int32_t table_ld, int32_t n_table_rows, const uint16_t* k_pool,
+                                  const uint16_t* v_pool, int32_t n_pages, uint16_t* out, int64_t ld_out,
+                                  void* stream) {
+    if (int rc = check_handle(h)) return rc;
+    DAP_REQUIRE(h->scratch, DAP_HIP_ERROR, "the handle has no static scratch address");
+    int dev = -1;
+    hipError_t e = hipGetDevice(&dev);
+    if (e != hipSuccess) return hip_fail(e, "hipGetDevice");
+    DAP_REQUIRE(dev == h->device, DAP_INVALID_ARG, "the handle's device must be current");
+    DAP_REQUIRE(n_rows >= 0 && n_rows <= dap::kMaxDecodeRows, n_rows < 0 ? DAP_INVALID_ARG : DAP_UNSUPPORTED,
+                "n_rows must lie in [0, 65535]");
+    const size_t need = dap_decode_workspace_bytes(h, n_rows);
+    if (need > kScratchBytes)
+        return fail(DAP_WORKSPACE_TOO_SMALL, "the decode's partials for " + std::to_string(n_rows) + " rows need " +
+                                                 std::to_string(need) + " bytes, above the static scratch of " +
+                                                 std::to_string(kScratchBytes) +
+                                                 " bytes; call dap_attn_decode_paged with a workspace");
+    return do_decode(h, q, ld_q, n_rows, positions, rows, table, table_ld, n_table_rows, k_pool, v_pool, n_pages, out,
+                     ld_out, h->scratch, kScratchBytes, static_cast<hipStream_t>(stream));
 }
 
 // Step workspace: the decode's partials, then the prefill's tile list.

@@ -200,6 +200,29 @@ int dap_attn_decode_paged(dap_handle* handle,
     void* workspace, size_t workspace_bytes, void* stream);
 
 /*
+ * The decode above without a workspace argument, for callers that cannot
+ * allocate device memory: code under HIP graph capture, tight serving loops,
+ * harnesses that forbid hipMalloc. The per-chunk partials go to a static
+ * device array of 32 MiB (33554432 bytes) inside the library instead; each
+ * GPU the library runs on holds its own copy from the first dap_create on it
+ * until the process ends. A call needing more than that
+ * (dap_decode_workspace_bytes(handle, n_rows) > 33554432, e.g. 8 rows at
+ * max_position 2^22 with 32 query heads) returns DAP_WORKSPACE_TOO_SMALL
+ * and launches nothing. Nothing is allocated or freed; no part of the
+ * scratch needs clearing (every partial is written before it is read).
+ * All calls on one GPU share the array: calls that overlap on one GPU (other
+ * streams, other threads, other handles) race and must be ordered by the
+ * caller. The handle's device must be current. Arguments and results are as
+ * for dap_attn_decode_paged.
+ */
+int dap_attn_decode_paged_noalloc(dap_handle* handle,
+    const uint16_t* q, int64_t ld_q, int32_t n_rows,
+    const int32_t* positions, const int32_t* rows,
+    const int32_t* table, int32_t table_ld, int32_t n_table_rows,
+    const uint16_t* k_pool, const uint16_t* v_pool, int32_t n_pages,
+    uint16_t* out, int64_t ld_out, void* stream);
+
+/*
  * One step over pages: packed prompts and one decode token per row in one
  * call. ("Mistral 7B Instruct v0.3", Entries: step_paged is prefill_paged
  * and decode_paged in one pass; "Phi-3 Mini 4K Instruct" files,
