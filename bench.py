@@ -113,6 +113,7 @@ class Bench:
                           + prefill_bytes(m, wl.pre_positions, wl.pre_segments))
             self.flops = prefill_flops(m, wl.pre_positions)
             self.dec_bytes = decode_bytes(m, wl.dec_positions)
+            self.pre_bytes = prefill_bytes(m, wl.pre_positions, wl.pre_segments)
             self.tokens = P + R
             self.desc = ("qwen3-4b-shaped step_paged: 2048 packed prefill tokens (8 prompts of 256, 4 sharing a "
                          "128-token prefix via shared pages) + 128 decode rows at p~U[512,40959], Hq32/Hkv8/D128, "
@@ -553,11 +554,20 @@ def main():
 
     m = b.m
     value = b.bytes / (ms_per_step * 1e-3) / 1e9
-    dom = max(("decode", "prefill", "write"), key=lambda k: prof[k][0])
+    dom = max(("decode", "prefill", "write", "step"), key=lambda k: prof[k][0])
     # totals over the profiled pass (args.steps steps; a step may hold many launches)
     total_ms = {k: v[0] for k, v in prof.items()}
     launches = {k: max(v[1], 1) for k, v in prof.items()}
-    if dom == "decode":
+    if dom == "step":
+        # step_paged's one launch for the prompts' tiles and the rows' chunks:
+        # bound by the decode's page reads (its MFMA work is a few GFLOP)
+        total = (b.dec_bytes + b.pre_bytes) * args.steps
+        achieved = total / (total_ms["step"] * 1e-3) / 1e9
+        roof = {"bound": "hbm", "achieved": round(achieved, 2), "peak": HBM_PEAK_GBS, "unit": "GB/s",
+                "frac": round(achieved / HBM_PEAK_GBS, 4), "kernel": "step_kernel",
+                "avg_launch_ms": round(kern_ms["step"], 5),
+                "algorithmic_bytes_per_launch": int(total // launches["step"])}
+    elif dom == "decode":
         total = b.dec_bytes * args.steps
         achieved = total / (total_ms["decode"] * 1e-3) / 1e9
         roof = {"bound": "hbm", "achieved": round(achieved, 2), "peak": HBM_PEAK_GBS, "unit": "GB/s",
@@ -594,14 +604,16 @@ def main():
         "cold_gbps": round(b.bytes / (float(np.median(cold_ms)) * 1e-3) / 1e9, 2),
         "hbm_copy_ceiling_gbps": copy_ceiling(),
     }
-    if b.flops:
+    if b.flops and prof["prefill"][1]:
         line["prefill_tflops"] = round(b.flops * args.steps / (total_ms["prefill"] * 1e-3) / 1e12, 2)
         line["prefill_frac_of_mfma_peak"] = round(line["prefill_tflops"] / BF16_PEAK_TFLOPS, 4)
+    if prof["step"][1]:
+        line["step_path"] = "one launch for the prompts' tiles and the rows' chunks (step_kernel)"
     if b.name == "qwen3":
         # the step's own prefill is 2048 short prompts (latency-bound): the
         # prefill half of the metric is measured on the long chunk
         line["prefill_packed"] = prefill_chunk_rate()
-    if b.dec_bytes:
+    if b.dec_bytes and prof["decode"][1]:
         g = b.dec_bytes * args.steps / (total_ms["decode"] * 1e-3) / 1e9
         line["decode_gbps"] = round(g, 2)
         line["decode_frac_of_hbm_peak"] = round(g / HBM_PEAK_GBS, 4)

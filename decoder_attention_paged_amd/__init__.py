@@ -31,7 +31,7 @@ EXPORTS = ("dap_create", "dap_destroy", "dap_last_error", "dap_set_validate", "d
            "dap_decode", "dap_decode_rows", "dap_prefill", "dap_prefill_slots", "dap_inpass_workspace_bytes",
            "dap_packed", "dap_forward", "dap_tile_layout")
 
-KERNELS = ("write", "prefill_tiles", "prefill", "decode", "decode_merge", "prep")
+KERNELS = ("write", "prefill_tiles", "prefill", "decode", "decode_merge", "prep", "step")
 
 
 class DapError(RuntimeError):

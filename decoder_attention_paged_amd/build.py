@@ -16,7 +16,7 @@ ROOT = os.path.dirname(PKG)
 CSRC = os.path.join(PKG, "csrc")
 BUILD = os.path.join(ROOT, "_build")
 LIB = os.path.join(PKG, "libdap.so")
-SOURCES = ["dap_api.hip", "rope_write.hip", "decode.hip", "prefill.hip", "prep.hip"]
+SOURCES = ["dap_api.hip", "rope_write.hip", "decode.hip", "prefill.hip", "prep.hip", "step.hip"]
 ARCH = "gfx950"
 
 # Packed fp32 instructions are disabled for every kernel on this target.

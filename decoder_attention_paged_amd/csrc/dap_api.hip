@@ -1,6 +1,7 @@
 // C-ABI layer: handle, argument checks, validate mode, launches.
 #include <cmath>
 #include <cstdio>
+#include <cstdlib>
 #include <cstring>
 #include <mutex>
 #include <string>
@@ -107,6 +108,7 @@ struct dap_handle {
     double* d_inv_freq;
     unsigned* d_err;
     int validate;
+    int one_pass_step;     // step_paged runs prompts and decode rows in one launch (DAP_FUSED_STEP=0: off)
     dap::ProfilerState* prof_state;
     dap::Profiler prof;
     dap::Profiler* profiler() { return prof_state ? &prof : nullptr; }
@@ -333,23 +335,20 @@ int attn_common_checks(dap_handle* h, const uint16_t* q, int64_t ld_q, const int
     return DAP_OK;
 }
 
-int do_prefill(dap_handle* h, const uint16_t* q, int64_t ld_q, int32_t n_tokens, const int32_t* positions,
-               const int32_t* segments, int32_t n_segments, const int32_t* table, int32_t table_ld,
-               int32_t n_table_rows, const uint16_t* k_pool, const uint16_t* v_pool, int32_t n_pages, uint16_t* out,
-               int64_t ld_out, void* workspace, size_t workspace_bytes, hipStream_t s) {
-    DAP_REQUIRE(n_tokens >= 0, DAP_INVALID_ARG, "n_tokens must be >= 0");
-    if (n_tokens == 0) return DAP_OK;
+// Checks of a packed prefill of n_tokens > 0 tokens launched as tile_blocks
+// workgroups (and, in validate mode, the host-side index checks). Nothing
+// is launched.
+int prefill_checks(dap_handle* h, const uint16_t* q, int64_t ld_q, int32_t n_tokens, const int32_t* positions,
+                   const int32_t* segments, int32_t n_segments, const int32_t* table, int32_t table_ld,
+                   int32_t n_table_rows, const uint16_t* k_pool, const uint16_t* v_pool, int32_t n_pages,
+                   const uint16_t* out, int64_t ld_out, long long tile_blocks, hipStream_t s) {
     DAP_REQUIRE(h->group == 1 || h->group == 2 || h->group == 4, DAP_UNSUPPORTED,
                 "prefill supports Hq/Hkv of 1, 2 or 4");
     if (int rc = attn_common_checks(h, q, ld_q, positions, table, table_ld, n_table_rows, k_pool, v_pool, n_pages, out, ld_out))
         return rc;
     DAP_REQUIRE(segments && aligned4(segments), DAP_INVALID_ARG, "segments must be a non-null aligned pointer");
     DAP_REQUIRE(n_segments > 0, DAP_INVALID_ARG, "n_segments must be positive");
-    const size_t need = dap::prefill_workspace(n_tokens, n_segments, h->group, h->m.head_dim);
-    DAP_REQUIRE(workspace && workspace_bytes >= need && aligned16(workspace), DAP_WORKSPACE_TOO_SMALL,
-                "workspace must be 16-byte aligned and at least dap_prefill_workspace_bytes()");
-    const long long blocks = (long long)dap::tile_cap(n_tokens, n_segments, h->group, h->m.head_dim) * h->m.n_kv_heads;
-    DAP_REQUIRE(blocks < (1ll << 31), DAP_UNSUPPORTED, "too many prefill tiles for one launch");
+    DAP_REQUIRE(tile_blocks < (1ll << 31), DAP_UNSUPPORTED, "too many prefill tiles for one launch");
     if (h->validate) {
         std::vector<int32_t> hp, hs, ht;
         if (!to_host(hp, positions, n_tokens, s) || !to_host(hs, segments, n_tokens, s) ||
@@ -359,8 +358,26 @@ int do_prefill(dap_handle* h, const uint16_t* q, int64_t ld_q, int32_t n_tokens,
         int runs = 0;
         for (int t = 0; t < n_tokens; ++t) runs += (t == 0 || hs[t] != hs[t - 1]);
         if (runs > n_segments) return fail(DAP_BAD_INDEX, "more runs of equal segment ids than n_segments");
-        if (int rc = begin_validate(h, s)) return rc;
     }
+    return DAP_OK;
+}
+
+int do_prefill(dap_handle* h, const uint16_t* q, int64_t ld_q, int32_t n_tokens, const int32_t* positions,
+               const int32_t* segments, int32_t n_segments, const int32_t* table, int32_t table_ld,
+               int32_t n_table_rows, const uint16_t* k_pool, const uint16_t* v_pool, int32_t n_pages, uint16_t* out,
+               int64_t ld_out, void* workspace, size_t workspace_bytes, hipStream_t s) {
+    DAP_REQUIRE(n_tokens >= 0, DAP_INVALID_ARG, "n_tokens must be >= 0");
+    if (n_tokens == 0) return DAP_OK;
+    const long long blocks =
+        n_segments > 0 ? (long long)dap::tile_cap(n_tokens, n_segments, h->group, h->m.head_dim) * h->m.n_kv_heads : 0;
+    if (int rc = prefill_checks(h, q, ld_q, n_tokens, positions, segments, n_segments, table, table_ld, n_table_rows,
+                                k_pool, v_pool, n_pages, out, ld_out, blocks, s))
+        return rc;
+    const size_t need = dap::prefill_workspace(n_tokens, n_segments, h->group, h->m.head_dim);
+    DAP_REQUIRE(workspace && workspace_bytes >= need && aligned16(workspace), DAP_WORKSPACE_TOO_SMALL,
+                "workspace must be 16-byte aligned and at least dap_prefill_workspace_bytes()");
+    if (h->validate)
+        if (int rc = begin_validate(h, s)) return rc;
     dap::AttnArgs a = attn_args(h, q, ld_q, n_tokens, positions, segments, table, table_ld, n_table_rows, k_pool,
                                 v_pool, n_pages, out, ld_out);
     hipError_t e = dap::launch_prefill(a, n_segments, workspace, s, h->profiler());
@@ -368,18 +385,17 @@ int do_prefill(dap_handle* h, const uint16_t* q, int64_t ld_q, int32_t n_tokens,
     return h->validate ? end_validate(h, s) : DAP_OK;
 }
 
-int do_decode(dap_handle* h, const uint16_t* q, int64_t ld_q, int32_t n_rows, const int32_t* positions,
-              const int32_t* rows, const int32_t* table, int32_t table_ld, int32_t n_table_rows,
-              const uint16_t* k_pool, const uint16_t* v_pool, int32_t n_pages, uint16_t* out, int64_t ld_out,
-              void* workspace, size_t workspace_bytes, hipStream_t s, const dap::WriteArgs* fused = nullptr) {
-    DAP_REQUIRE(n_rows >= 0, DAP_INVALID_ARG, "n_rows must be >= 0");
-    if (n_rows == 0) return DAP_OK;
+// Checks of a decode of n_rows > 0 rows (and, in validate mode, the host
+// index checks); returns its plan in `plan`. Nothing is launched.
+int decode_checks(dap_handle* h, const uint16_t* q, int64_t ld_q, int32_t n_rows, const int32_t* positions,
+                  const int32_t* rows, const int32_t* table, int32_t table_ld, int32_t n_table_rows,
+                  const uint16_t* k_pool, const uint16_t* v_pool, int32_t n_pages, const uint16_t* out, int64_t ld_out,
+                  size_t workspace_bytes, const void* workspace, dap::DecodePlan& plan, hipStream_t s) {
     DAP_REQUIRE(n_rows <= dap::kMaxDecodeRows, DAP_UNSUPPORTED, "at most 65535 rows per decode call");
     if (int rc = attn_common_checks(h, q, ld_q, positions, table, table_ld, n_table_rows, k_pool, v_pool, n_pages, out, ld_out))
         return rc;
     DAP_REQUIRE(!rows || aligned4(rows), DAP_INVALID_ARG, "rows must be aligned");
-    const dap::DecodePlan plan = dap::decode_plan(n_rows, h->m.n_q_heads, h->m.n_kv_heads, h->m.head_dim,
-                                                  h->m.window, h->m.max_position);
+    plan = dap::decode_plan(n_rows, h->m.n_q_heads, h->m.n_kv_heads, h->m.head_dim, h->m.window, h->m.max_position);
     DAP_REQUIRE(dap::decode_plan_fits(plan), DAP_UNSUPPORTED, "decode split plan beyond the kernel's limits");
     DAP_REQUIRE(workspace && workspace_bytes >= plan.workspace_bytes && aligned16(workspace), DAP_WORKSPACE_TOO_SMALL,
                 "workspace must be 16-byte aligned and at least dap_decode_workspace_bytes()");
@@ -391,8 +407,22 @@ int do_decode(dap_handle* h, const uint16_t* q, int64_t ld_q, int32_t n_rows, co
             !to_host(ht, table, (size_t)table_ld * n_table_rows, s))
             return fail(DAP_HIP_ERROR, "copying index arrays");
         if (int rc = check_rows(h, hp, hr, ht, table_ld, n_table_rows, n_pages, true, nullptr)) return rc;
-        if (int rc = begin_validate(h, s)) return rc;
     }
+    return DAP_OK;
+}
+
+int do_decode(dap_handle* h, const uint16_t* q, int64_t ld_q, int32_t n_rows, const int32_t* positions,
+              const int32_t* rows, const int32_t* table, int32_t table_ld, int32_t n_table_rows,
+              const uint16_t* k_pool, const uint16_t* v_pool, int32_t n_pages, uint16_t* out, int64_t ld_out,
+              void* workspace, size_t workspace_bytes, hipStream_t s, const dap::WriteArgs* fused = nullptr) {
+    DAP_REQUIRE(n_rows >= 0, DAP_INVALID_ARG, "n_rows must be >= 0");
+    if (n_rows == 0) return DAP_OK;
+    dap::DecodePlan plan;
+    if (int rc = decode_checks(h, q, ld_q, n_rows, positions, rows, table, table_ld, n_table_rows, k_pool, v_pool,
+                               n_pages, out, ld_out, workspace_bytes, workspace, plan, s))
+        return rc;
+    if (h->validate)
+        if (int rc = begin_validate(h, s)) return rc;
     dap::AttnArgs a = attn_args(h, q, ld_q, n_rows, positions, rows, table, table_ld, n_table_rows, k_pool, v_pool,
                                 n_pages, out, ld_out);
     hipError_t e = dap::launch_decode(a, plan, workspace, s, h->profiler(), fused);
@@ -412,6 +442,45 @@ bool fuse_decode(const dap_handle* h, int32_t n_rows) {
     const dap::DecodePlan plan = dap::decode_plan(n_rows, h->m.n_q_heads, h->m.n_kv_heads, h->m.head_dim,
                                                   h->m.window, h->m.max_position);
     return (long long)plan.max_splits * h->m.n_kv_heads * n_rows <= kFusedDecodeMaxBlocks;
+}
+
+// step_paged with both prompt tokens and decode rows, in one attention
+// launch: every check first (nothing runs if one fails), then the write of
+// every token, then the prompts' tiles and the rows' chunks together (one
+// kernel), then the decode's merge. The prefill workgroups there find their
+// own tiles by scanning the prompts' segment ids, which stays cheap up to a
+// few thousand prompt tokens; longer prompt parts take the separate launches.
+constexpr int kOnePassMaxPrompt = 4096;
+
+int do_step_one_pass(dap_handle* h, const dap::WriteArgs& wa, int32_t n_prompt, int32_t n_segments, int32_t n_step,
+                     const int32_t* positions, const int32_t* rows, const int32_t* table, int32_t table_ld,
+                     int32_t n_table_rows, const uint16_t* k_pool, const uint16_t* v_pool, int32_t n_pages,
+                     uint16_t* out, int64_t ld_out, void* dec_ws, size_t dec_bytes, hipStream_t s) {
+    const uint16_t* q_out = wa.q_out;
+    const int64_t ld_q = wa.ld_q_out;
+    const long long pre_blocks =
+        n_segments > 0 ? (long long)dap::step_tile_cap(n_prompt, n_segments, h->group) * h->m.n_kv_heads : 0;
+    if (int rc = prefill_checks(h, q_out, ld_q, n_prompt, positions, rows, n_segments, table, table_ld, n_table_rows,
+                                k_pool, v_pool, n_pages, out, ld_out, pre_blocks, s))
+        return rc;
+    dap::DecodePlan plan;
+    const uint16_t* q_step = q_out + (int64_t)n_prompt * ld_q;
+    uint16_t* out_step = out + (int64_t)n_prompt * ld_out;
+    if (int rc = decode_checks(h, q_step, ld_q, n_step, positions + n_prompt, rows + n_prompt, table, table_ld,
+                               n_table_rows, k_pool, v_pool, n_pages, out_step, ld_out, dec_bytes, dec_ws, plan, s))
+        return rc;
+    DAP_REQUIRE(pre_blocks + (long long)plan.max_splits * h->m.n_kv_heads * n_step < (1ll << 31), DAP_UNSUPPORTED,
+                "too many workgroups for one launch");
+    if (int rc = launch_write_checked(h, wa, s)) return rc;
+    if (h->validate)
+        if (int rc = begin_validate(h, s)) return rc;
+    const dap::AttnArgs pre = attn_args(h, q_out, ld_q, n_prompt, positions, rows, table, table_ld, n_table_rows,
+                                        k_pool, v_pool, n_pages, out, ld_out);
+    const dap::AttnArgs dec = attn_args(h, q_step, ld_q, n_step, positions + n_prompt, rows + n_prompt, table,
+                                        table_ld, n_table_rows, k_pool, v_pool, n_pages, out_step, ld_out);
+    hipError_t e = dap::launch_step(pre, n_segments, dec, plan, dec_ws, s, h->profiler());
+    if (e != hipSuccess) return hip_fail(e, "step launch");
+    return h->validate ? end_validate(h, s) : DAP_OK;
 }
 
 // ---------------------------------------------------------------- contiguous-cache and in-pass entries
@@ -690,6 +759,10 @@ int dap_create(const dap_model* mp, dap_handle** out) {
     h->m = m;
     h->group = m.n_q_heads / m.n_kv_heads;
     h->validate = 0;
+    {
+        const char* env = std::getenv("DAP_FUSED_STEP");
+        h->one_pass_step = !(env && env[0] == '0');
+    }
     h->d_inv_freq = nullptr;
     h->d_err = nullptr;
     h->prof_state = nullptr;
@@ -863,13 +936,18 @@ int dap_step_paged(dap_handle* h, const uint16_t* q, const uint16_t* k, const ui
     if (int rc = write_args(h, q, k, v, ld_in, n_prompt + n_step, positions, rows, slots, table, table_ld,
                             n_table_rows, q_gain, k_gain, q_out, ld_q_out, k_pool, v_pool, n_pages, wa, s))
         return rc;
-    // In order on `stream`: every token's write, the prompts' prefill, then
-    // the decode. (The prompt part on a second stream beside the decode was
-    // measured equal or slower: their workgroups cannot share a CU.) A call
-    // with no prompt tokens skips the write launch: the decode writes each
-    // row's token itself (K, V and q_out, from the workgroup that reads the
-    // token's page) before reading it. That needs q_out apart from q (the
-    // decode's workgroups read q while q_out is written).
+    // With both prompt tokens (up to kOnePassMaxPrompt) and decode rows: the
+    // write, then the prompts' tiles and the rows' chunks in one launch.
+    // Otherwise in order on `stream`: every token's write, the prompts'
+    // prefill, then the decode. A call with no prompt tokens skips the write
+    // launch: the decode writes each row's token itself (K, V and q_out,
+    // from the workgroup that reads the token's page) before reading it.
+    // That needs q_out apart from q (the decode's workgroups read q while
+    // q_out is written).
+    if (h->one_pass_step && n_prompt > 0 && n_step > 0 && n_prompt <= kOnePassMaxPrompt &&
+        (h->group == 1 || h->group == 2 || h->group == 4))
+        return do_step_one_pass(h, wa, n_prompt, n_segments, n_step, positions, rows, table, table_ld, n_table_rows,
+                                k_pool, v_pool, n_pages, out, ld_out, workspace, dec_bytes, s);
     const bool fused = n_prompt == 0 && n_step > 0 && q_out != q && fuse_decode(h, n_step);
     if (fused && h->validate) {
         std::vector<int32_t> hr;

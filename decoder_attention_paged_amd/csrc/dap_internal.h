@@ -19,7 +19,7 @@ enum ErrorBits : unsigned {
     kErrPage = 4u,
     kErrSlot = 8u,
     kErrTable = 16u,
-    // 32 is the prefill's segment-run overflow (prefill.hip)
+    kErrSegments = 32u,  // more runs of equal segment ids than the prefill launch has tiles for
     kErrSpan = 64u,      // an in-pass segment's positions do not fit its scratch pages
 };
 
@@ -53,6 +53,11 @@ typedef float f32x4 __attribute__((ext_vector_type(4)));
 typedef float f32x16 __attribute__((ext_vector_type(16)));
 typedef unsigned u32x4 __attribute__((ext_vector_type(4)));
 
+typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
+constexpr bf16x2 kOnes2 = {(__bf16)1.0f, (__bf16)1.0f};   // dot2 with this adds a pair
+constexpr float kLog2e = 1.4426950408889634f;
+
+__device__ __forceinline__ bf16x8 as_bf16x8(u32x4 u) { return __builtin_bit_cast(bf16x8, u); }
 __device__ __forceinline__ float bf16_to_f32(uint32_t b) { return __uint_as_float(b << 16); }
 
 // float32 -> bf16, round to nearest even; NaN stays a quiet NaN.
@@ -145,6 +150,19 @@ struct AttnArgs {
 // from the raw projection, in the workgroups that read the token's page
 hipError_t launch_decode(const AttnArgs& a, const DecodePlan& plan, void* workspace, hipStream_t s,
                          Profiler* prof, const WriteArgs* fused = nullptr);
+
+// the cross-chunk merge alone (rows of several chunks), after a decode whose
+// partials are in `workspace`
+hipError_t launch_decode_merge(const AttnArgs& a, const DecodePlan& plan, void* workspace, hipStream_t s,
+                               Profiler* prof);
+
+// Fused step: the packed prefill's tiles (pre, its tokens) and the decode's
+// chunks (dec, its rows) in one launch, then the decode's merge. Each prefill
+// workgroup finds its own tile (no tile-list pass); pre.n_tokens > 0 and
+// dec.n_tokens > 0, group 1, 2 or 4.
+int step_tile_cap(int n_prompt, int n_segments, int group);     // prefill workgroup slots per kv head
+hipError_t launch_step(const AttnArgs& pre, int n_segments, const AttnArgs& dec, const DecodePlan& plan,
+                       void* workspace, hipStream_t s, Profiler* prof);
 
 // Prefill: tile list sizing and launch.
 size_t prefill_workspace(int n_tokens, int n_segments, int group, int head_dim);

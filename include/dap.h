@@ -385,7 +385,8 @@ enum {
     DAP_KERNEL_DECODE = 3,         /* the decode kernel */
     DAP_KERNEL_DECODE_MERGE = 4,   /* the decode's cross-chunk merge */
     DAP_KERNEL_PREP = 5,           /* index preparation of the contiguous and in-pass entries */
-    DAP_N_KERNELS = 6
+    DAP_KERNEL_STEP = 6,           /* step_paged's fused prefill tiles and decode chunks */
+    DAP_N_KERNELS = 7
 };
 int dap_set_profiling(dap_handle* handle, int on);
 int dap_profile_read(dap_handle* handle, double* total_ms, int64_t* launches, int reset);
