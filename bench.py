@@ -485,17 +485,20 @@ def cold_steps(b: "Bench", n: int, flush_bytes: int = 512 << 20) -> np.ndarray:
 # --------------------------------------------------------------------------- traffic counters
 def traffic_for(kernel: str, workload: str):
     """HBM bytes per launch from the committed rocprofv3 counter summary,
-    null when absent or taken on a different kernel source."""
+    null when absent or taken on different kernel sources (the summary holds
+    the SHA-256 of every source file the kernel is compiled from)."""
     path = os.path.join(PROFILES, f"{kernel}_{workload}_counters.json")
     if not os.path.exists(path):
         return None
     with open(path) as fh:
         rec = json.load(fh)
-    src = os.path.join(ROOT, "decoder_attention_paged_amd", "csrc", rec.get("source", ""))
-    if not os.path.exists(src):
-        return None
-    digest = hashlib.sha256(open(src, "rb").read()).hexdigest()
-    if digest != rec.get("source_sha256"):
+    h = hashlib.sha256()
+    for name in rec.get("sources", []):
+        src = os.path.join(ROOT, "decoder_attention_paged_amd", "csrc", name)
+        if not os.path.exists(src):
+            return None
+        h.update(open(src, "rb").read())
+    if not rec.get("sources") or h.hexdigest() != rec.get("sources_sha256"):
         return None
     return rec.get("bytes_per_launch", {}).get("total")
 
