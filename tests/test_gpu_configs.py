@@ -85,7 +85,8 @@ def test_phi3_prefill_then_decode_loop():
         qo = h.rope_qknorm_write_pages(*_split(x, m), tp, kp, vp, rows=tr, table=table)
         o = h.attn_decode_paged(qo, tp, table, kp, vp, rows=tr, workspace=ws)
         if t in sample_steps:
-            kept[t] = (x.clone(), o.clone())
+            o4 = h.attn_decode_paged(_peaky(qo), tp, table, kp, vp, rows=tr, workspace=ws)
+            kept[t] = (x.clone(), o.clone(), o4.clone())
         all_tok.append((t, rows, positions))
     torch.cuda.synchronize()
     # the oracle writes every decode token (its own k/v) and checks sampled steps
@@ -96,8 +97,10 @@ def test_phi3_prefill_then_decode_loop():
         op.write(s, kb, vb)
         if t in kept:
             assert np.array_equal(to_np_bits(kept[t][0]), x)
-            ref = oracle_attention(wl, op, bf16.to_f64(qb), positions, rows)
+            qf = bf16.to_f64(qb)
+            ref, ref4 = oracle_rows(wl, op, [qf, 4 * qf], positions, rows)
             check_close(to_np_bits(kept[t][1]), ref, f"phi3 decode step {t}")
+            check_close(to_np_bits(kept[t][2]), ref4, f"phi3 decode step {t}, peaky")
     # read-only measurement call: all four rows at 3000
     q = W.normal_matrix(wl.key("q", "final"), 4, m.n_q_heads * m.head_dim, "cuda")
     p3000 = np.full(4, 3000, np.int32)
