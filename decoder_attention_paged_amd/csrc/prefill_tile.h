@@ -13,7 +13,10 @@
 // reference max, and with it O, moves only when a score passes it by more
 // than 2^8, so the weights stay at most 256). Pages fully outside a wave's
 // rows are skipped; only pages that straddle a row's causal or window edge
-// are masked element by element.
+// are masked element by element. With eight waves (one workgroup per CU)
+// each wave's fragment reads run beside its MFMAs, one read per MFMA (page
+// j's V^T fragments beside its score MFMAs, page j+1's K fragments beside
+// its PV MFMAs), so no wave waits for a page's K fragments after the barrier.
 //
 // Sources: "Phi-3 Mini 4K Instruct" files, src/attention.linnet
 // (prefill_packed: token i sees token j iff they share a segment and
@@ -153,18 +156,18 @@ __device__ __forceinline__ void prefill_tile(const AttnArgs& a, int t0, int t1, 
             kmin = min(kmin, a.window > 0 ? max(0, pp - a.window + 1) : 0);
         }
     }
-    kmin = wave_min(kmin);
-    kmax = wave_max(kmax);
+    kmin = __builtin_amdgcn_readfirstlane(wave_min(kmin));
+    kmax = __builtin_amdgcn_readfirstlane(wave_max(kmax));
     if (kmax < 0) return;                        // uniform: no valid token
     if ((kmax >> 6) >= a.table_ld) {
         if (tid == 0 && kh == 0) atomicOr(a.err, kErrTable);
         return;
     }
-    // this wave's rows
-    const int w_pmax = wave_max(p);
-    const int w_lomin = wave_min(lo);
-    const int w_pmin = wave_min(row_valid && p >= 0 ? p : (1 << 30));
-    const int w_lomax = wave_max(row_valid && p >= 0 ? lo : -1);
+    // this wave's rows (the same in every lane: scalar registers and branches)
+    const int w_pmax = __builtin_amdgcn_readfirstlane(wave_max(p));
+    const int w_lomin = __builtin_amdgcn_readfirstlane(wave_min(lo));
+    const int w_pmin = __builtin_amdgcn_readfirstlane(wave_min(row_valid && p >= 0 ? p : (1 << 30)));
+    const int w_lomax = __builtin_amdgcn_readfirstlane(wave_max(row_valid && p >= 0 ? lo : -1));
 
     // Q^T as the B operand: column = query row, k-group = dims 16s + 8*half
     bf16x8 qf[kSteps];
@@ -239,67 +242,30 @@ __device__ __forceinline__ void prefill_tile(const AttnArgs& a, int t0, int t1, 
         else __builtin_amdgcn_s_waitcnt(waitcnt_vmcnt(0));
     };
 
-    // Pipeline over NB buffers: page j is computed from buffer (j - j_first)
-    // % NB while pages j+1 .. j+NB-1 load; the loads of page j+NB-1 start
-    // right after the barrier that ends every wave's reads of page j-1 (whose
-    // buffer they overwrite). One barrier per page.
-    unsigned okbits = 0;                 // bit k: page j+k has a valid id
-    int b_issue = 0, b_cur = 0;
-    for (int jj = j_first; jj <= j_last && jj <= j_first + NB - 2; ++jj) {
-        okbits |= (unsigned)issue(page_id(jj), b_issue) << (jj - j_first);
-        b_issue = b_issue + 1 == NB ? 0 : b_issue + 1;
-    }
-    int pg_next = j_first + NB - 1 <= j_last ? page_id(j_first + NB - 1) : -1;
-
-    for (int j = j_first; j <= j_last; ++j) {
-        wait_loads(min(NB - 2, j_last - j));
-        __builtin_amdgcn_s_barrier();
-        asm volatile("" ::: "memory");
-        // every wave has read page j-1: its buffer takes the loads of page j+NB-1
-        if (j + NB - 1 <= j_last) {
-            okbits |= (unsigned)issue(pg_next, b_issue) << (NB - 1);
-            b_issue = b_issue + 1 == NB ? 0 : b_issue + 1;
-            if (j + NB <= j_last) pg_next = page_id(j + NB);
-        }
-        const bool ok_cur = okbits & 1u;
-        okbits >>= 1;
-        // fragment f of this page: fr[64 * f]; K (blk, s) is f = blk * kSteps + s,
-        // V^T (t, db) is f = kFragK + t * kDimBlocks + db
-        const u32x4* fr = s_buf + b_cur * (kBufBytes / 16) + lane;
-        b_cur = b_cur + 1 == NB ? 0 : b_cur + 1;
-        const int k0 = j * kPage;
-        if (!ok_cur && tid == 0 && kh == 0) atomicOr(a.err, kErrPage);
-        if (ok_cur && !(k0 > w_pmax || k0 + kPage - 1 < w_lomin)) {   // skip pages invisible to this wave
-        // S^T = K Q^T : two 32-key blocks. All K fragments are read from LDS
-        // first (they return in order, so the MFMAs then issue back to back);
-        // the scheduling barrier keeps the compiler from pairing each read
-        // with its MFMA, which would expose the LDS latency every time.
-        u32x4 kf[2][kSteps];
+    typedef f32x16 Scores[2];
+    typedef u32x4 VFrags[4][kDimBlocks];
+    typedef u32x4 KFrags[2][kSteps];
+    // K fragment (32-key block blk, k-step s) and V^T fragment (16-key step
+    // t, dim block db) of the page whose buffer starts at fr (lane-offset)
+    auto kfrag = [&](const u32x4* fr, int blk, int s) { return fr[64 * (blk * kSteps + s)]; };
+    auto vfrag = [&](const u32x4* fr, int t, int db) { return fr[64 * (kFragK + t * kDimBlocks + db)]; };
+    // S^T = K Q^T for one page: two 32-key blocks of kSteps MFMAs each,
+    // unscaled (the scale folds into the exp2 argument); the two blocks'
+    // accumulation chains alternate so consecutive MFMAs are independent
+    auto scores = [&](const KFrags& kf, Scores& sc) __attribute__((always_inline)) {
 #pragma unroll
         for (int blk = 0; blk < 2; ++blk)
 #pragma unroll
-            for (int s = 0; s < kSteps; ++s) kf[blk][s] = fr[64 * (blk * kSteps + s)];
-        __builtin_amdgcn_sched_barrier(0);
-        f32x16 sc[2];
+            for (int r = 0; r < 16; ++r) sc[blk][r] = 0.f;
 #pragma unroll
-        for (int blk = 0; blk < 2; ++blk) {
-            f32x16 acc;
+        for (int s = 0; s < kSteps; ++s)
 #pragma unroll
-            for (int r = 0; r < 16; ++r) acc[r] = 0.f;
-#pragma unroll
-            for (int s = 0; s < kSteps; ++s)
-                acc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(as_bf16x8(kf[blk][s]), qf[s], acc, 0, 0, 0);
-            sc[blk] = acc;                     // unscaled; the scale folds into the exp2 argument
-        }
-        // V^T fragments for the PV step, read now so their latency hides
-        // under the softmax below
-        u32x4 vfr[4][kDimBlocks];
-#pragma unroll
-        for (int t = 0; t < 4; ++t)
-#pragma unroll
-            for (int db = 0; db < kDimBlocks; ++db)
-                vfr[t][db] = fr[64 * (kFragK + t * kDimBlocks + db)];
-        __builtin_amdgcn_sched_barrier(0);
+            for (int blk = 0; blk < 2; ++blk)
+                sc[blk] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(as_bf16x8(kf[blk][s]), qf[s], sc[blk], 0, 0, 0);
+    };
+    // The masks of a page starting at key k0, then its softmax weights in
+    // place of the scores.
+    auto weights = [&](int k0, Scores& sc, VFrags& vfr) __attribute__((always_inline)) {
         // mask where this page crosses an edge of some row's range
         if (k0 < w_lomax || k0 + kPage - 1 > w_pmin) {
 #pragma unroll
@@ -362,25 +328,163 @@ __device__ __forceinline__ void prefill_tile(const AttnArgs& a, int t0, int t1, 
 #pragma unroll
             for (int r = 0; r < 16; ++r)
                 sc[blk][r] = __builtin_amdgcn_exp2f(__builtin_fmaf(sc[blk][r], c, -m_ref));
+    };
+    // bf16 weights of 16-key step t (the P^T operand) from the float ones
+    auto pfrag = [&](const Scores& sc, int t) {
+        bf16x8 pf;
+#pragma unroll
+        for (int e = 0; e < 8; ++e) pf[e] = (__bf16)sc[t >> 1][8 * (t & 1) + e];
+        return pf;
+    };
+    // The row sum adds the bf16 weights the MFMAs use, two per dot2 (the
+    // normaliser is then the sum of exactly the weights applied to V).
+    auto add_sums = [&](const bf16x8& pf, float& ps0, float& ps1) {
+        ps0 = __builtin_amdgcn_fdot2_f32_bf16(__builtin_shufflevector(pf, pf, 0, 1), kOnes2, ps0, false);
+        ps1 = __builtin_amdgcn_fdot2_f32_bf16(__builtin_shufflevector(pf, pf, 2, 3), kOnes2, ps1, false);
+        ps0 = __builtin_amdgcn_fdot2_f32_bf16(__builtin_shufflevector(pf, pf, 4, 5), kOnes2, ps0, false);
+        ps1 = __builtin_amdgcn_fdot2_f32_bf16(__builtin_shufflevector(pf, pf, 6, 7), kOnes2, ps1, false);
+    };
 
-        // O^T += V^T P^T : four 16-key steps. The row sum adds the bf16
-        // weights the MFMAs use, two per dot2 (the normaliser is then the sum
-        // of exactly the weights applied to V).
+    // Streamed steps of one page (eight waves; see below).
+    auto read_k = [&](const u32x4* frk, KFrags& kf) __attribute__((always_inline)) {
+#pragma unroll
+        for (int blk = 0; blk < 2; ++blk)
+#pragma unroll
+            for (int s = 0; s < kSteps; ++s) kf[blk][s] = kfrag(frk, blk, s);
+    };
+    auto read_v = [&](const u32x4* fr, VFrags& vfr) __attribute__((always_inline)) {
+#pragma unroll
+        for (int t = 0; t < 4; ++t)
+#pragma unroll
+            for (int db = 0; db < kDimBlocks; ++db) vfr[t][db] = vfrag(fr, t, db);
+    };
+    // score MFMAs, each followed by one V^T fragment read of the page (into
+    // the registers the MFMAs free)
+    auto score_stream = [&](const KFrags& kf, const u32x4* fr, Scores& sc, VFrags& vfr)
+        __attribute__((always_inline)) {
+        __builtin_amdgcn_sched_barrier(0);
+        scores(kf, sc);
+        read_v(fr, vfr);
+#pragma unroll
+        for (int i = 0; i < 2 * kSteps; ++i) {
+            __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);    // one MFMA
+            __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);    // one LDS read
+        }
+        __builtin_amdgcn_sched_barrier(0);
+    };
+    // the softmax of a scored page, then its PV MFMAs, each followed by one
+    // K fragment read from frk (the page to score next)
+    auto soft_pv_stream = [&](int k0, Scores& sc, VFrags& vfr, const u32x4* frk, KFrags& kf)
+        __attribute__((always_inline)) {
+        weights(k0, sc, vfr);
+        bf16x8 pf[4];
         float ps0 = 0.f, ps1 = 0.f;
 #pragma unroll
         for (int t = 0; t < 4; ++t) {
-            bf16x8 pf;
-#pragma unroll
-            for (int e = 0; e < 8; ++e) pf[e] = (__bf16)sc[t >> 1][8 * (t & 1) + e];
-#pragma unroll
-            for (int db = 0; db < kDimBlocks; ++db)
-                o[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(as_bf16x8(vfr[t][db]), pf, o[db], 0, 0, 0);
-            ps0 = __builtin_amdgcn_fdot2_f32_bf16(__builtin_shufflevector(pf, pf, 0, 1), kOnes2, ps0, false);
-            ps1 = __builtin_amdgcn_fdot2_f32_bf16(__builtin_shufflevector(pf, pf, 2, 3), kOnes2, ps1, false);
-            ps0 = __builtin_amdgcn_fdot2_f32_bf16(__builtin_shufflevector(pf, pf, 4, 5), kOnes2, ps0, false);
-            ps1 = __builtin_amdgcn_fdot2_f32_bf16(__builtin_shufflevector(pf, pf, 6, 7), kOnes2, ps1, false);
+            pf[t] = pfrag(sc, t);
+            add_sums(pf[t], ps0, ps1);
         }
         lsum += ps0 + ps1;
+        __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+        for (int t = 0; t < 4; ++t)
+#pragma unroll
+            for (int db = 0; db < kDimBlocks; ++db)
+                o[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(as_bf16x8(vfr[t][db]), pf[t], o[db], 0, 0, 0);
+        read_k(frk, kf);
+#pragma unroll
+        for (int i = 0; i < 4 * kDimBlocks; ++i) {
+            __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+            __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
+        }
+        __builtin_amdgcn_sched_barrier(0);
+    };
+
+    // Pipeline over NB buffers: page j is read from buffer (j - j_first) %
+    // NB; after the barrier that opens page j the loads of page j+NB-1
+    // start, into the buffer of page j-1, which every wave has finished
+    // with. One barrier per page.
+    //
+    // Streamed form (eight waves, one workgroup per CU): the fragment reads
+    // are spread over the matrix work instead of every wave reading a page's
+    // K fragments at once after the barrier while the matrix units wait. The
+    // barrier before page j also certifies that page j+1 has landed (each
+    // wave first waits for its own loads of both; loads then lead their use
+    // by two pages). A wave reads the V^T fragments of page j while its
+    // score MFMAs of page j run, and the K fragments of page j+1 while its PV
+    // MFMAs of page j run, one read per MFMA into the registers the MFMAs
+    // free.
+    constexpr bool kStream = W == 8 && NB >= 4;
+    constexpr int kLead = NB - 1;
+    unsigned okbits = 0;                 // bit k: page j+k has a valid id
+    int b_issue = 0, b_cur = 0;
+    for (int jj = j_first; jj <= j_last && jj < j_first + kLead; ++jj) {
+        okbits |= (unsigned)issue(page_id(jj), b_issue) << (jj - j_first);
+        b_issue = b_issue + 1 == NB ? 0 : b_issue + 1;
+    }
+    int pg_next = j_first + kLead <= j_last ? page_id(j_first + kLead) : -1;
+    KFrags kf;                           // streamed form: K fragments of the page to score next
+
+    for (int j = j_first; j <= j_last; ++j) {
+        // in flight after the wait: the loads of pages past j (past j+1 when streamed)
+        wait_loads(kStream ? max(0, min(kLead - 2, j_last - j - 1)) : min(kLead - 1, j_last - j));
+        __builtin_amdgcn_s_barrier();
+        asm volatile("" ::: "memory");
+        if (j + kLead <= j_last) {
+            okbits |= (unsigned)issue(pg_next, b_issue) << kLead;
+            b_issue = b_issue + 1 == NB ? 0 : b_issue + 1;
+            if (j + kLead + 1 <= j_last) pg_next = page_id(j + kLead + 1);
+        }
+        const bool ok_cur = okbits & 1u;
+        okbits >>= 1;
+        const u32x4* fr = s_buf + b_cur * (kBufBytes / 16) + lane;
+        b_cur = b_cur + 1 == NB ? 0 : b_cur + 1;
+        const u32x4* fr_next = s_buf + b_cur * (kBufBytes / 16) + lane;   // page j+1
+        const int k0 = j * kPage;
+        if (!ok_cur && tid == 0 && kh == 0) atomicOr(a.err, kErrPage);
+        // pages invisible to this wave's rows are skipped
+        const bool vis = __builtin_amdgcn_readfirstlane(
+            (int)(ok_cur && !(k0 > w_pmax || k0 + kPage - 1 < w_lomin)));
+
+        if constexpr (kStream) {
+            // After the last page the K reads still run (from a buffer no
+            // load writes any more, values unused) so the fragments are
+            // defined on every path round the loop.
+            if (j == j_first) read_k(fr, kf);
+            if (vis) {
+                Scores scj;
+                VFrags vfr;
+                score_stream(kf, fr, scj, vfr);
+                soft_pv_stream(k0, scj, vfr, fr_next, kf);
+            } else {
+                read_k(fr_next, kf);
+            }
+        } else if (vis) {
+            // All K fragments are read from LDS first (they return in order,
+            // so the MFMAs then issue back to back); the scheduling barrier
+            // keeps the compiler from pairing each read with its MFMA, which
+            // would expose the LDS latency every time.
+            read_k(fr, kf);
+            __builtin_amdgcn_sched_barrier(0);
+            Scores scj;
+            scores(kf, scj);
+            // V^T fragments for the PV step, read now so their latency
+            // hides under the softmax below
+            VFrags vfr;
+            read_v(fr, vfr);
+            __builtin_amdgcn_sched_barrier(0);
+            weights(k0, scj, vfr);
+            // O^T += V^T P^T : four 16-key steps
+            float ps0 = 0.f, ps1 = 0.f;
+#pragma unroll
+            for (int t = 0; t < 4; ++t) {
+                const bf16x8 pf = pfrag(scj, t);
+#pragma unroll
+                for (int db = 0; db < kDimBlocks; ++db)
+                    o[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(as_bf16x8(vfr[t][db]), pf, o[db], 0, 0, 0);
+                add_sums(pf, ps0, ps1);
+            }
+            lsum += ps0 + ps1;
         }
     }
 
