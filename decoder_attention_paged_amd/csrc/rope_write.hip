@@ -192,7 +192,9 @@ __global__ __launch_bounds__(kWriteThreads, 4) void rope_write_token_kernel(Writ
             load_item<D>(a, t, (it0 + b) * kWriteThreads + tid, n_rope_heads, lo[b], hi[b], head[b], j[b],
                          active[b]);
         if (it0 == 0) {                                       // uniform: the angle table, once
-            if (tid == 0) s_slot = token_slot(a, t, p, true);
+            // the slot lookup (two dependent loads) in the last wave, the
+            // angle table in the first
+            if (tid == kWriteThreads - 64) s_slot = token_slot(a, t, p, true);
             angle_table<D>(a.inv_freq, p, tid, kWriteThreads, s_cos, s_sin);
             __syncthreads();
             slot = s_slot;
