@@ -71,34 +71,35 @@ def _bf16_ulp(x):
 
 @pytest.mark.parametrize("peaky", [False, True])
 def test_decode_rows_indirection_and_split_invariance(peaky):
-    """The same rows decoded with one chunk per row, two, eight and sixteen
-    (the chunk size follows the call's size, so the rows are repeated 16, 8,
-    2 and 1 times), and under other handles' chunkings. The merge is exact in
-    real arithmetic and the decode applies each weight with 16 significant
-    bits (a bf16 pair), so every chunking must agree with the one-chunk
-    result to float32 rounding, and every result must lie within one bf16
-    ulp (plus 2^-20 for float32 cancellation) of the fp64 oracle."""
+    """The same rows decoded with one chunk per row, two, four and sixteen
+    for the longest row (the chunk size follows the call's size, so the rows
+    are repeated 32, 16, 8, 2 and 1 times), and under other handles'
+    chunkings. The merge is exact in real arithmetic and the decode applies
+    each weight with 16 significant bits (a bf16 pair), so every chunking
+    must agree with the one-chunk result to float32 rounding, and every
+    result must lie within one bf16 ulp (plus 2^-20 for float32
+    cancellation) of the fp64 oracle."""
     model = _model(32, 8, 128, 0, max_position=65536)
-    wl = _workload(model, 8, 64, "dec-rows")
+    wl = _workload(model, 8, 128, "dec-rows")
     kp, vp = device_pools(wl)
     rows = np.array([7, 2, 2, 5], np.int32)
-    positions = np.array([4095, 4000, 130, 64], np.int32)
+    positions = np.array([8191, 4000, 130, 64], np.int32)
     q = _queries(wl, 4, 4.0 if peaky else 1.0)
     h = handle_for(model)
     results = {}
-    for rep in (16, 8, 2, 1):           # 1, 2, 8 and 16 chunks for the 64-page row
+    for rep in (32, 16, 8, 2, 1):       # 1, 2, 4, 16 and 16 chunks for the 128-page row
         n = 4 * rep
         # the chunk size, from the library's workspace query: n rows x Hq x
         # chunks per row (for the longest row, 1024 pages) x (D + 2) floats
         splits = h.decode_workspace_bytes(n) // (n * 32 * 130 * 4)
-        chunks = -(-64 // (1024 // splits))
+        chunks = -(-128 // (1024 // splits))
         out = h.attn_decode_paged(q.repeat(rep, 1), torch_i32(np.tile(positions, rep)), torch_i32(wl.table), kp, vp,
                                   rows=torch_i32(np.tile(rows, rep)))
         o = to_np_bits(out).reshape(rep, 4, -1)
         assert all(np.array_equal(o[0], o[i]) for i in range(rep)), "repeated rows differ within one call"
         results[chunks] = o[0]
-    assert sorted(results) == [1, 2, 8, 16], sorted(results)
-    for max_pos in (4096, 1 << 20):                  # other handles, other chunkings
+    assert sorted(results) == [1, 2, 4, 16], sorted(results)
+    for max_pos in (8192, 1 << 20):                  # other handles, other chunkings
         h2 = handle_for(_model(32, 8, 128, 0, max_position=max_pos))
         out = h2.attn_decode_paged(q, torch_i32(positions), torch_i32(wl.table), kp, vp, rows=torch_i32(rows))
         results[f"max_position {max_pos}"] = to_np_bits(out)
