@@ -43,7 +43,8 @@ __global__ __launch_bounds__(kDecodeThreads, 2) void decode_kernel(AttnArgs a, i
 template <int D>
 __global__ __launch_bounds__(kDecodeThreads) void decode_merge_kernel(AttnArgs a, int pps, int max_splits,
                                                                       const float* __restrict__ ws) {
-    __shared__ float s_w[kMaxSplits * 16];     // per (chunk, head): 2^(m_s - M)
+    __shared__ float s_w[kMaxSplits * 16];     // per (chunk, head): m_s, then 2^(m_s - M)
+    __shared__ float s_l[kMaxSplits * 16];     // per (chunk, head): l_s
     __shared__ float s_inv_l[16];
     const int kh = blockIdx.x;
     const int b = blockIdx.y;
@@ -56,8 +57,13 @@ __global__ __launch_bounds__(kDecodeThreads) void decode_merge_kernel(AttnArgs a
     const long long slot0 = ((long long)b * a.n_kv_heads + kh) * max_splits;
     const float* part_o = ws + slot0 * G * D;
     const float* part_ml = ws + (long long)a.n_tokens * a.n_kv_heads * max_splits * G * D + slot0 * G * 2;
-    // every chunk's m in parallel, then per head the max, the weights and 1/L
-    for (int i = tid; i < n_splits * G; i += kDecodeThreads) s_w[i] = part_ml[2 * i];
+    // every chunk's (m, l) in parallel, then per head the max, the weights
+    // and 1/L from LDS
+    for (int i = tid; i < n_splits * G; i += kDecodeThreads) {
+        const float2 ml = *reinterpret_cast<const float2*>(part_ml + 2 * i);
+        s_w[i] = ml.x;
+        s_l[i] = ml.y;
+    }
     __syncthreads();
     if (tid < G) {
         float M = -INFINITY;
@@ -66,7 +72,7 @@ __global__ __launch_bounds__(kDecodeThreads) void decode_merge_kernel(AttnArgs a
         for (int sp = 0; sp < n_splits; ++sp) {
             const float w = M == -INFINITY ? 0.f : exp2f(s_w[sp * G + tid] - M);
             s_w[sp * G + tid] = w;
-            L += w * part_ml[2 * (sp * G + tid) + 1];
+            L += w * s_l[sp * G + tid];
         }
         s_inv_l[tid] = L > 0.f ? 1.f / L : 0.f;
     }
@@ -74,13 +80,29 @@ __global__ __launch_bounds__(kDecodeThreads) void decode_merge_kernel(AttnArgs a
     for (int item = tid; item < G * D; item += kDecodeThreads) {
         const int j = item / D;
         const float* src = part_o + item;
+        // four accumulators, chunk sp into accumulator sp % 4; eight chunks'
+        // loads in flight together
         float ov0 = 0.f, ov1 = 0.f, ov2 = 0.f, ov3 = 0.f;
         int sp = 0;
-        for (; sp + 4 <= n_splits; sp += 4) {   // independent loads in flight together
+        for (; sp + 8 <= n_splits; sp += 8) {
+            float x[8];
+#pragma unroll
+            for (int u = 0; u < 8; ++u) x[u] = src[(long long)(sp + u) * G * D];
+            ov0 += s_w[sp * G + j] * x[0];
+            ov1 += s_w[(sp + 1) * G + j] * x[1];
+            ov2 += s_w[(sp + 2) * G + j] * x[2];
+            ov3 += s_w[(sp + 3) * G + j] * x[3];
+            ov0 += s_w[(sp + 4) * G + j] * x[4];
+            ov1 += s_w[(sp + 5) * G + j] * x[5];
+            ov2 += s_w[(sp + 6) * G + j] * x[6];
+            ov3 += s_w[(sp + 7) * G + j] * x[7];
+        }
+        if (sp + 4 <= n_splits) {
             ov0 += s_w[sp * G + j] * src[(long long)sp * G * D];
             ov1 += s_w[(sp + 1) * G + j] * src[(long long)(sp + 1) * G * D];
             ov2 += s_w[(sp + 2) * G + j] * src[(long long)(sp + 2) * G * D];
             ov3 += s_w[(sp + 3) * G + j] * src[(long long)(sp + 3) * G * D];
+            sp += 4;
         }
         for (; sp < n_splits; ++sp) ov0 += s_w[sp * G + j] * src[(long long)sp * G * D];
         const float ov = (ov0 + ov1) + (ov2 + ov3);
