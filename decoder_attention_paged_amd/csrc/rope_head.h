@@ -86,16 +86,19 @@ __device__ __forceinline__ void rope_chunk_pair(const WriteArgs& a, bool is_q, i
         ss += __shfl_xor(ss, 2);
         ss += __shfl_xor(ss, 4);
         if (active) {
-            const double denom = sqrt(ss / (double)D + a.eps);
+            // one reciprocal instead of a division per element: the float64
+            // value moves by an ulp or so, which changes the bf16 rounding
+            // only at a rounding near-tie
+            const double inv = 1.0 / sqrt(ss / (double)D + a.eps);
             const uint16_t* g = is_q ? a.q_gain : a.k_gain;
             const u32x4 gl = *reinterpret_cast<const u32x4*>(g + 8 * j);
             const u32x4 gh = *reinterpret_cast<const u32x4*>(g + kHalf + 8 * j);
 #pragma unroll
             for (int w = 0; w < 4; ++w) {
-                xl[2 * w] = (double)bf16_to_f32(gl[w] & 0xffffu) * xl[2 * w] / denom;
-                xl[2 * w + 1] = (double)bf16_to_f32(gl[w] >> 16) * xl[2 * w + 1] / denom;
-                xh[2 * w] = (double)bf16_to_f32(gh[w] & 0xffffu) * xh[2 * w] / denom;
-                xh[2 * w + 1] = (double)bf16_to_f32(gh[w] >> 16) * xh[2 * w + 1] / denom;
+                xl[2 * w] = (double)bf16_to_f32(gl[w] & 0xffffu) * xl[2 * w] * inv;
+                xl[2 * w + 1] = (double)bf16_to_f32(gl[w] >> 16) * xl[2 * w + 1] * inv;
+                xh[2 * w] = (double)bf16_to_f32(gh[w] & 0xffffu) * xh[2 * w] * inv;
+                xh[2 * w + 1] = (double)bf16_to_f32(gh[w] >> 16) * xh[2 * w + 1] * inv;
             }
         }
     }
