@@ -611,6 +611,9 @@ struct InpassLayout {
     int32_t* table;
     int32_t* slots;
     int32_t* rel;
+    int32_t* seg_lo;      // per-segment scratch of the preparation
+    int32_t* seg_hi;
+    int32_t* seg_first;
     uint16_t* q_rope;
     char* prefill;
     uint16_t* k_pool;
@@ -630,6 +633,9 @@ InpassLayout inpass_layout(const dap_handle* h, void* ws, long long n_tokens, in
     L.table = c.take<int32_t>((size_t)n_segments * L.table_ld);
     L.slots = c.take<int32_t>(n_tokens);
     L.rel = c.take<int32_t>(n_tokens);
+    L.seg_lo = c.take<int32_t>(n_segments);
+    L.seg_hi = c.take<int32_t>(n_segments);
+    L.seg_first = c.take<int32_t>(n_segments);
     L.q_rope = c.take<uint16_t>((size_t)n_tokens * h->m.n_q_heads * h->m.head_dim);
     L.prefill = c.base ? c.base + c.off : nullptr;
     c.off += align256(dap::prefill_workspace((int)n_tokens, n_segments, h->group, h->m.head_dim));
@@ -715,6 +721,9 @@ int do_inpass(dap_handle* h, const uint16_t* q, const uint16_t* k, const uint16_
     ip.capacity = L.capacity;
     ip.slots = L.slots;
     ip.rel_positions = L.rel;
+    ip.seg_lo = L.seg_lo;
+    ip.seg_hi = L.seg_hi;
+    ip.seg_first = L.seg_first;
     ip.err = h->d_err;
     hipError_t e = dap::launch_inpass_prep(ip, s, h->profiler());
     if (e != hipSuccess) return hip_fail(e, "in-pass preparation launch");

@@ -204,6 +204,9 @@ struct InpassPrep {
     int capacity;           // scratch pages
     int32_t* slots;         // [n_tokens] scratch slot of each token, -1 if it does not fit
     int32_t* rel_positions; // [n_tokens] position minus its segment's first position
+    int32_t* seg_lo;        // [n_segments] scratch: each segment's first position,
+    int32_t* seg_hi;        //   last position
+    int32_t* seg_first;     //   and first scratch page
     unsigned* err;
 };
 hipError_t launch_inpass_prep(const InpassPrep& p, hipStream_t s, Profiler* prof);

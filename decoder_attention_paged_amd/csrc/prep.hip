@@ -53,73 +53,81 @@ __global__ __launch_bounds__(kLayoutThreads) void layout_prep_kernel(LayoutPrep 
     }
 }
 
-// One workgroup: per-segment first and last positions (LDS atomics), page
-// counts, an exclusive scan for each segment's first scratch page, then the
-// table and every token's scratch slot.
-__global__ __launch_bounds__(kInpassThreads) void inpass_prep_kernel(InpassPrep p) {
-    __shared__ int s_lo[kMaxInpassSegments];
-    __shared__ int s_hi[kMaxInpassSegments];
-    __shared__ int s_first[kMaxInpassSegments];
+// In-pass preparation, four launches: (1) each segment's bounds set to
+// empty, (2) every segment's first and last positions by global atomics
+// from many workgroups (one update per wave whose tokens share a segment,
+// the usual case since segments are runs of the pack), (3) one workgroup
+// turns the bounds into page counts and an exclusive scan, each segment's
+// first scratch page, (4) every token's scratch slot and relative position
+// and every table entry.
+constexpr int kInpassRounds = 4;                                   // tokens per thread in the bounds pass
+constexpr int kBoundsThreads = 256;
+constexpr int kBoundsTokens = kBoundsThreads * kInpassRounds;     // tokens per bounds workgroup
+
+__global__ __launch_bounds__(kLayoutThreads) void inpass_init_kernel(InpassPrep p) {
+    const int s = blockIdx.x * kLayoutThreads + threadIdx.x;
+    if (s < p.n_segments) {
+        p.seg_lo[s] = 0x7fffffff;
+        p.seg_hi[s] = -1;
+    }
+}
+
+__global__ __launch_bounds__(kBoundsThreads) void inpass_bounds_kernel(InpassPrep p) {
+    const int lane = threadIdx.x & 63;
+    const int ns = p.n_segments;
+    // a wave takes 64 consecutive tokens per round; every round's tokens are
+    // loaded before any is used
+    const int base = blockIdx.x * kBoundsTokens + (threadIdx.x - lane) * kInpassRounds;
+    int sgs[kInpassRounds], poss[kInpassRounds];
+#pragma unroll
+    for (int k = 0; k < kInpassRounds; ++k) {
+        const int t = base + 64 * k + lane;
+        sgs[k] = t < p.n_tokens ? p.segments[t] : -1;
+        poss[k] = t < p.n_tokens ? p.positions[t] : 0;
+    }
+#pragma unroll
+    for (int k = 0; k < kInpassRounds; ++k) {
+        const int t = base + 64 * k + lane;
+        if (base + 64 * k >= p.n_tokens) break;               // uniform: no token left in this round
+        const bool valid = t < p.n_tokens;
+        const int sg = sgs[k], pos = poss[k];
+        const int s0 = __builtin_amdgcn_readfirstlane(sg);    // lane 0 holds a token
+        if (__ballot(valid && sg != s0) == 0 && s0 >= 0 && s0 < ns) {   // uniform
+            int lo = valid ? pos : 0x7fffffff, hi = valid ? pos : -1;
+#pragma unroll
+            for (int o = 32; o > 0; o >>= 1) {
+                lo = min(lo, __shfl_xor(lo, o));
+                hi = max(hi, __shfl_xor(hi, o));
+            }
+            if (lane == 0) {
+                atomicMin(&p.seg_lo[s0], lo);
+                atomicMax(&p.seg_hi[s0], hi);
+            }
+            continue;
+        }
+        if (!valid) continue;
+        if (sg < 0 || sg >= ns) {
+            atomicOr(p.err, kErrRow);
+            continue;
+        }
+        atomicMin(&p.seg_lo[sg], pos);
+        atomicMax(&p.seg_hi[sg], pos);
+    }
+}
+
+// pages per segment and their exclusive scan: each segment's first scratch page
+__global__ __launch_bounds__(kInpassThreads) void inpass_scan_kernel(InpassPrep p) {
     __shared__ int s_part[kInpassThreads];
     const int tid = threadIdx.x;
     const int ns = p.n_segments;
-    for (int s = tid; s < ns; s += kInpassThreads) {
-        s_lo[s] = 0x7fffffff;
-        s_hi[s] = -1;
-    }
-    __syncthreads();
-    // A wave whose tokens all lie in one segment (the usual case: segments
-    // are runs of the pack) reduces their positions by shuffles and makes
-    // one update; otherwise each lane updates its own segment. Four rounds'
-    // tokens are loaded before any is used, to keep loads in flight.
-    constexpr int kRounds = 4;
-    const int lane = tid & 63;
-    for (int tb = tid - lane; tb < p.n_tokens; tb += kRounds * kInpassThreads) {
-        int sgs[kRounds], poss[kRounds];
-#pragma unroll
-        for (int k = 0; k < kRounds; ++k) {
-            const int t = tb + k * kInpassThreads + lane;
-            sgs[k] = t < p.n_tokens ? p.segments[t] : -1;
-            poss[k] = t < p.n_tokens ? p.positions[t] : 0;
-        }
-#pragma unroll
-        for (int k = 0; k < kRounds; ++k) {
-            const int t = tb + k * kInpassThreads + lane;
-            const bool valid = t < p.n_tokens;
-            const int sg = sgs[k], pos = poss[k];
-            if (tb + k * kInpassThreads >= p.n_tokens) break;     // uniform: no token left in this round
-            const int s0 = __builtin_amdgcn_readfirstlane(sg);  // lane 0 holds a token
-            if (__ballot(valid && sg != s0) == 0 && s0 >= 0 && s0 < ns) {   // uniform
-                int lo = valid ? pos : 0x7fffffff, hi = valid ? pos : -1;
-#pragma unroll
-                for (int o = 32; o > 0; o >>= 1) {
-                    lo = min(lo, __shfl_xor(lo, o));
-                    hi = max(hi, __shfl_xor(hi, o));
-                }
-                if (lane == 0) {
-                    atomicMin(&s_lo[s0], lo);
-                    atomicMax(&s_hi[s0], hi);
-                }
-                continue;
-            }
-            if (!valid) continue;
-            if (sg < 0 || sg >= ns) {
-                atomicOr(p.err, kErrRow);
-                continue;
-            }
-            atomicMin(&s_lo[sg], pos);
-            atomicMax(&s_hi[sg], pos);
-        }
-    }
-    __syncthreads();
-    // pages per segment, exclusive scan (each thread owns a run of segments)
-    constexpr int kPer = kMaxInpassSegments / kInpassThreads;
+    constexpr int kPer = kMaxInpassSegments / kInpassThreads;      // each thread owns a run of segments
     int cnt[kPer];
     int sum = 0;
 #pragma unroll
     for (int k = 0; k < kPer; ++k) {
         const int s = tid * kPer + k;
-        cnt[k] = (s < ns && s_hi[s] >= 0) ? (s_hi[s] - s_lo[s]) / kPage + 1 : 0;
+        const int hi = s < ns ? p.seg_hi[s] : -1;
+        cnt[k] = hi >= 0 ? (hi - p.seg_lo[s]) / kPage + 1 : 0;
         sum += cnt[k];
     }
     s_part[tid] = sum;
@@ -134,43 +142,41 @@ __global__ __launch_bounds__(kInpassThreads) void inpass_prep_kernel(InpassPrep 
 #pragma unroll
     for (int k = 0; k < kPer; ++k) {
         const int s = tid * kPer + k;
-        if (s < ns) s_first[s] = run;
+        if (s < ns) p.seg_first[s] = run;
         run += cnt[k];
     }
-    __syncthreads();
-    // table rows: page j of segment s, if it exists and fits
+}
+
+// every token's scratch slot and relative position, and every table entry
+// (page j of segment s, if it exists and fits)
+__global__ __launch_bounds__(kLayoutThreads) void inpass_slots_kernel(InpassPrep p) {
+    const int ns = p.n_segments;
     const long long n_table = (long long)ns * p.table_ld;
-    for (long long i = tid; i < n_table; i += kInpassThreads) {
-        const int s = (int)(i / p.table_ld), j = (int)(i % p.table_ld);
-        const int pages = s_hi[s] >= 0 ? (s_hi[s] - s_lo[s]) / kPage + 1 : 0;
-        const int pg = s_first[s] + j;
-        p.table[i] = (j < pages && pg < p.capacity) ? pg : -1;
-    }
-    for (int tb = tid; tb < p.n_tokens; tb += kRounds * kInpassThreads) {
-        int sgs[kRounds], poss[kRounds];
-#pragma unroll
-        for (int k = 0; k < kRounds; ++k) {
-            const int t = tb + k * kInpassThreads;
-            sgs[k] = t < p.n_tokens ? p.segments[t] : -1;
-            poss[k] = t < p.n_tokens ? p.positions[t] : 0;
-        }
-#pragma unroll
-        for (int k = 0; k < kRounds; ++k) {
-            const int t = tb + k * kInpassThreads;
-            if (t >= p.n_tokens) break;
-            const int sg = sgs[k];
+    const long long n = n_table > p.n_tokens ? n_table : p.n_tokens;
+    for (long long i = blockIdx.x * (long long)kLayoutThreads + threadIdx.x; i < n;
+         i += (long long)gridDim.x * kLayoutThreads) {
+        if (i < p.n_tokens) {
+            const int t = (int)i;
+            const int sg = p.segments[t];
             if (sg < 0 || sg >= ns) {
                 p.slots[t] = -1;
                 p.rel_positions[t] = 0;
-                continue;
+            } else {
+                const int rel = p.positions[t] - p.seg_lo[sg];
+                const int j = rel / kPage;
+                const int pg = p.seg_first[sg] + j;
+                const bool fits = j < p.table_ld && pg < p.capacity;
+                if (!fits) atomicOr(p.err, kErrSpan);
+                p.slots[t] = fits ? pg * kPage + rel % kPage : -1;
+                p.rel_positions[t] = rel;
             }
-            const int rel = poss[k] - s_lo[sg];
-            const int j = rel / kPage;
-            const int pg = s_first[sg] + j;
-            const bool fits = j < p.table_ld && pg < p.capacity;
-            if (!fits) atomicOr(p.err, kErrSpan);
-            p.slots[t] = fits ? pg * kPage + rel % kPage : -1;
-            p.rel_positions[t] = rel;
+        }
+        if (i < n_table) {
+            const int s = (int)(i / p.table_ld), j = (int)(i % p.table_ld);
+            const int hi = p.seg_hi[s];
+            const int pages = hi >= 0 ? (hi - p.seg_lo[s]) / kPage + 1 : 0;
+            const int pg = p.seg_first[s] + j;
+            p.table[i] = (j < pages && pg < p.capacity) ? pg : -1;
         }
     }
 }
@@ -192,8 +198,17 @@ hipError_t launch_layout_prep(const LayoutPrep& p, hipStream_t s, Profiler* prof
 hipError_t launch_inpass_prep(const InpassPrep& p, hipStream_t s, Profiler* prof) {
     if (p.n_tokens <= 0) return hipSuccess;
     if (p.n_segments <= 0 || p.n_segments > kMaxInpassSegments) return hipErrorInvalidValue;
+    const long long n_table = (long long)p.n_segments * p.table_ld;
+    const long long n = n_table > p.n_tokens ? n_table : p.n_tokens;
+    const long long slot_blocks = (n + kLayoutThreads - 1) / kLayoutThreads;
     if (prof) prof->begin(DAP_KERNEL_PREP, s);
-    hipLaunchKernelGGL(inpass_prep_kernel, dim3(1), dim3(kInpassThreads), 0, s, p);
+    hipLaunchKernelGGL(inpass_init_kernel, dim3((p.n_segments + kLayoutThreads - 1) / kLayoutThreads),
+                       dim3(kLayoutThreads), 0, s, p);
+    hipLaunchKernelGGL(inpass_bounds_kernel, dim3((p.n_tokens + kBoundsTokens - 1) / kBoundsTokens),
+                       dim3(kBoundsThreads), 0, s, p);
+    hipLaunchKernelGGL(inpass_scan_kernel, dim3(1), dim3(kInpassThreads), 0, s, p);
+    hipLaunchKernelGGL(inpass_slots_kernel, dim3((unsigned)(slot_blocks < 4096 ? slot_blocks : 4096)),
+                       dim3(kLayoutThreads), 0, s, p);
     if (prof) prof->end(DAP_KERNEL_PREP, s);
     return hipGetLastError();
 }
