@@ -136,6 +136,25 @@ def test_packed_segments_at_their_own_positions(name):
     check_close(to_np_bits(out), _inpass_ref(wl, qkv, positions, segments, g_np), f"packed {name}")
 
 
+def test_packed_many_segments_across_workgroups():
+    """300 segments of 1-40 tokens at scattered starting positions: segment
+    bounds gathered by several preparation workgroups, most waves spanning
+    more than one segment, segments straddling wave and workgroup edges."""
+    m = MODELS["gqa2-d64"]
+    wl = W.Workload("pk-many", m, 1, np.zeros((1, 1), np.int32))
+    h = handle_for(m, validate=True)
+    rng = np.random.default_rng(20250)
+    lens = rng.integers(1, 41, size=300)
+    starts = rng.integers(0, 1024 - 40, size=300)
+    positions = np.concatenate([np.arange(a, a + n, dtype=np.int32) for a, n in zip(starts, lens)])
+    segments = np.concatenate([np.full(n, s, np.int32) for s, n in enumerate(lens)])
+    assert len(positions) > 4 * 1024          # more than four preparation workgroups of tokens
+    qkv = wl.qkv("many", len(positions), "cuda")
+    out = h.packed(*_split(qkv, m), torch_i32(positions), torch_i32(segments), n_segments=300)
+    torch.cuda.synchronize()
+    check_close(to_np_bits(out), _inpass_ref(wl, qkv, positions, segments, None), "packed, 300 segments")
+
+
 def test_packed_equals_prompts_alone_and_reuses_its_workspace():
     m = MODELS["gqa4-d128-qknorm"]
     wl = W.Workload("pk-alone", m, 1, np.zeros((1, 1), np.int32))
