@@ -14,9 +14,11 @@
 // than 2^8, so the weights stay at most 256). Pages fully outside a wave's
 // rows are skipped; only pages that straddle a row's causal or window edge
 // are masked element by element. With eight waves (one workgroup per CU)
-// each wave's fragment reads run beside its MFMAs, one read per MFMA (page
-// j's V^T fragments beside its score MFMAs, page j+1's K fragments beside
-// its PV MFMAs), so no wave waits for a page's K fragments after the barrier.
+// each wave's fragment reads run beside its MFMAs (page j's V^T fragments
+// beside its score MFMAs, page j+1's K fragments beside the second half of
+// its PV MFMAs), so no wave waits for a page's K fragments after the
+// barrier, and half of each page's exps run beside the first half of its
+// PV MFMAs.
 //
 // Sources: "Phi-3 Mini 4K Instruct" files, src/attention.linnet
 // (prefill_packed: token i sees token j iff they share a segment and
@@ -265,7 +267,7 @@ __device__ __forceinline__ void prefill_tile(const AttnArgs& a, int t0, int t1, 
     };
     // The masks of a page starting at key k0, then its softmax weights in
     // place of the scores.
-    auto weights = [&](int k0, Scores& sc, VFrags& vfr) __attribute__((always_inline)) {
+    auto weights = [&](int k0, Scores& sc, VFrags& vfr, bool exps = true) __attribute__((always_inline)) {
         // mask where this page crosses an edge of some row's range
         if (k0 < w_lomax || k0 + kPage - 1 > w_pmin) {
 #pragma unroll
@@ -322,6 +324,7 @@ __device__ __forceinline__ void prefill_tile(const AttnArgs& a, int t0, int t1, 
             for (int db = 0; db < kDimBlocks; ++db) o[db] *= alpha;
             if (move) m = ms;
         }
+        if (!exps) return;
         const float m_ref = m == -INFINITY ? 0.f : m;     // a row with nothing visible yet
 #pragma unroll
         for (int blk = 0; blk < 2; ++blk)
@@ -344,6 +347,8 @@ __device__ __forceinline__ void prefill_tile(const AttnArgs& a, int t0, int t1, 
         ps0 = __builtin_amdgcn_fdot2_f32_bf16(__builtin_shufflevector(pf, pf, 4, 5), kOnes2, ps0, false);
         ps1 = __builtin_amdgcn_fdot2_f32_bf16(__builtin_shufflevector(pf, pf, 6, 7), kOnes2, ps1, false);
     };
+
+    constexpr bool kStream = W == 8 && NB >= 4;   // the streamed form (see the page loop)
 
     // Streamed steps of one page (eight waves; see below).
     auto read_k = [&](const u32x4* frk, KFrags& kf) __attribute__((always_inline)) {
@@ -372,32 +377,51 @@ __device__ __forceinline__ void prefill_tile(const AttnArgs& a, int t0, int t1, 
         }
         __builtin_amdgcn_sched_barrier(0);
     };
-    // the softmax of a scored page, then its PV MFMAs, each followed by one
-    // K fragment read from frk (the page to score next)
-    auto soft_pv_stream = [&](int k0, Scores& sc, VFrags& vfr, const u32x4* frk, KFrags& kf)
+    // Streamed form: the softmax of a scored page and its PV MFMAs, split at
+    // the page's two 32-key blocks so that half of the exps run beside
+    // MFMAs: block 0's weights first, then its PV MFMAs, each with two of
+    // block 1's exps beside it, then block 1's PV MFMAs, each with two K
+    // fragment reads of the page to score next (from frk, in the order its
+    // score MFMAs use them; the first half's V fragments are free by then).
+    // One chunk per MFMA, kept in order by scheduling barriers. The weights,
+    // sums and products are the same operations in the same order as
+    // weights() followed by the four 16-key steps.
+    auto soft_pv = [&](int k0, Scores& sc, VFrags& vfr, const u32x4* frk, KFrags& kf)
         __attribute__((always_inline)) {
-        weights(k0, sc, vfr);
+        weights(k0, sc, vfr, false);                      // masks, row max, reference move
+        const float nm = -(m == -INFINITY ? 0.f : m);
         bf16x8 pf[4];
         float ps0 = 0.f, ps1 = 0.f;
 #pragma unroll
-        for (int t = 0; t < 4; ++t) {
-            pf[t] = pfrag(sc, t);
+        for (int t = 0; t < 2; ++t) {
+#pragma unroll
+            for (int e = 0; e < 8; ++e)
+                pf[t][e] = (__bf16)__builtin_amdgcn_exp2f(__builtin_fmaf(sc[0][8 * t + e], c, nm));
             add_sums(pf[t], ps0, ps1);
         }
-        lsum += ps0 + ps1;
         __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
-        for (int t = 0; t < 4; ++t)
+        for (int i = 0; i < 2 * kDimBlocks; ++i) {
+            const int t = i / kDimBlocks, db = i % kDimBlocks;
+            o[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(as_bf16x8(vfr[t][db]), pf[t], o[db], 0, 0, 0);
 #pragma unroll
-            for (int db = 0; db < kDimBlocks; ++db)
-                o[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(as_bf16x8(vfr[t][db]), pf[t], o[db], 0, 0, 0);
-        read_k(frk, kf);
-#pragma unroll
-        for (int i = 0; i < 4 * kDimBlocks; ++i) {
-            __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
-            __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
+            for (int x = (16 * i) / (2 * kDimBlocks); x < (16 * (i + 1)) / (2 * kDimBlocks); ++x)
+                pf[2 + x / 8][x % 8] = (__bf16)__builtin_amdgcn_exp2f(__builtin_fmaf(sc[1][x], c, nm));
+            __builtin_amdgcn_sched_barrier(0);
         }
-        __builtin_amdgcn_sched_barrier(0);
+        add_sums(pf[2], ps0, ps1);
+        add_sums(pf[3], ps0, ps1);
+        lsum += ps0 + ps1;
+#pragma unroll
+        for (int i = 2 * kDimBlocks; i < 4 * kDimBlocks; ++i) {
+            const int t = i / kDimBlocks, db = i % kDimBlocks;
+            o[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(as_bf16x8(vfr[t][db]), pf[t], o[db], 0, 0, 0);
+            const int r = i - 2 * kDimBlocks;
+#pragma unroll
+            for (int x = (2 * kSteps * r) / (2 * kDimBlocks); x < (2 * kSteps * (r + 1)) / (2 * kDimBlocks); ++x)
+                kf[x & 1][x >> 1] = kfrag(frk, x & 1, x >> 1);
+            __builtin_amdgcn_sched_barrier(0);
+        }
     };
 
     // Pipeline over NB buffers: page j is read from buffer (j - j_first) %
@@ -414,7 +438,6 @@ __device__ __forceinline__ void prefill_tile(const AttnArgs& a, int t0, int t1, 
     // score MFMAs of page j run, and the K fragments of page j+1 while its PV
     // MFMAs of page j run, one read per MFMA into the registers the MFMAs
     // free.
-    constexpr bool kStream = W == 8 && NB >= 4;
     constexpr int kLead = NB - 1;
     unsigned okbits = 0;                 // bit k: page j+k has a valid id
     int b_issue = 0, b_cur = 0;
@@ -455,7 +478,7 @@ __device__ __forceinline__ void prefill_tile(const AttnArgs& a, int t0, int t1, 
                 Scores scj;
                 VFrags vfr;
                 score_stream(kf, fr, scj, vfr);
-                soft_pv_stream(k0, scj, vfr, fr_next, kf);
+                soft_pv(k0, scj, vfr, fr_next, kf);
             } else {
                 read_k(fr_next, kf);
             }
@@ -474,7 +497,8 @@ __device__ __forceinline__ void prefill_tile(const AttnArgs& a, int t0, int t1, 
             read_v(fr, vfr);
             __builtin_amdgcn_sched_barrier(0);
             weights(k0, scj, vfr);
-            // O^T += V^T P^T : four 16-key steps
+            // O^T += V^T P^T : four 16-key steps (the split of soft_pv measured
+            // 1 % slower here, with two four-wave workgroups per CU)
             float ps0 = 0.f, ps1 = 0.f;
 #pragma unroll
             for (int t = 0; t < 4; ++t) {
