@@ -75,8 +75,8 @@ __global__ __launch_bounds__(kLayoutThreads) void inpass_init_kernel(InpassPrep 
 __global__ __launch_bounds__(kBoundsThreads) void inpass_bounds_kernel(InpassPrep p) {
     const int lane = threadIdx.x & 63;
     const int ns = p.n_segments;
-    // a wave takes 64 consecutive tokens per round; every round's tokens are
-    // loaded before any is used
+    // a wave takes kInpassRounds groups of 64 consecutive tokens (group k at
+    // base + 64 k); every group's tokens are loaded before any is used
     const int base = blockIdx.x * kBoundsTokens + (threadIdx.x - lane) * kInpassRounds;
     int sgs[kInpassRounds], poss[kInpassRounds];
 #pragma unroll
@@ -88,7 +88,7 @@ __global__ __launch_bounds__(kBoundsThreads) void inpass_bounds_kernel(InpassPre
 #pragma unroll
     for (int k = 0; k < kInpassRounds; ++k) {
         const int t = base + 64 * k + lane;
-        if (base + 64 * k >= p.n_tokens) break;               // uniform: no token left in this round
+        if (base + 64 * k >= p.n_tokens) break;               // uniform: this wave has no token at k
         const bool valid = t < p.n_tokens;
         const int sg = sgs[k], pos = poss[k];
         const int s0 = __builtin_amdgcn_readfirstlane(sg);    // lane 0 holds a token
