@@ -155,6 +155,40 @@ def test_packed_many_segments_across_workgroups():
     check_close(to_np_bits(out), _inpass_ref(wl, qkv, positions, segments, None), "packed, 300 segments")
 
 
+@pytest.mark.parametrize("seed", range(6))
+def test_random_packed_matches_oracle(seed):
+    """Seeded random in-pass calls: head_dim 64/96/128, 1-8 kv heads, 1, 2 or
+    4 query heads per kv head, a window or none, QK-norm or none, llama3
+    rope or not; 1-20 segments of 1-200 tokens packed in a shuffled id order
+    at scattered first positions, three segment ids left empty."""
+    rng = np.random.default_rng(3000 + seed)
+    D = int(rng.choice([64, 96, 128]))
+    hkv = int(rng.choice([1, 2, 4, 8]))
+    g = int(rng.choice([1, 2, 4]))
+    window = int(rng.choice([0, 0, 1, 37, 200]))
+    llama3 = (8.0, 1.0, 4.0, 8192.0) if rng.random() < 0.3 else None
+    eps = 1e-6 if rng.random() < 0.4 else None
+    theta = float(rng.choice([1e4, 5e5, 1e6]))
+    m = W.ModelShape(f"pk-rand-{seed}", hkv * g, hkv, D, theta, window=window, llama3=llama3, qk_norm_eps=eps,
+                     max_position=2048)
+    wl = W.Workload(m.name, m, 1, np.zeros((1, 1), np.int32))
+    n_seg = int(rng.integers(1, 21))
+    ids = rng.permutation(n_seg + 3)[:n_seg]            # three ids stay empty
+    lens = rng.integers(1, 201, size=n_seg)
+    starts = rng.integers(0, 2048 - 200, size=n_seg)
+    positions = np.concatenate([np.arange(a, a + n, dtype=np.int32) for a, n in zip(starts, lens)])
+    segments = np.concatenate([np.full(n, sid, np.int32) for sid, n in zip(ids, lens)])
+    h = handle_for(m, validate=True)
+    qg, kg, g_np = _gains(wl)
+    qkv = wl.qkv("rand", len(positions), "cuda")
+    out = h.packed(*_split(qkv, m), torch_i32(positions), torch_i32(segments), n_segments=n_seg + 3, q_gain=qg,
+                   k_gain=kg)
+    torch.cuda.synchronize()
+    check_close(to_np_bits(out), _inpass_ref(wl, qkv, positions, segments, g_np),
+                f"packed seed {seed} ({hkv * g}/{hkv}/{D} w{window} norm {eps} llama3 {llama3 is not None}, "
+                f"{n_seg} segments)")
+
+
 def test_packed_equals_prompts_alone_and_reuses_its_workspace():
     m = MODELS["gqa4-d128-qknorm"]
     wl = W.Workload("pk-alone", m, 1, np.zeros((1, 1), np.int32))
