@@ -8,6 +8,15 @@ if ROOT not in sys.path:
     sys.path.insert(0, ROOT)
 
 
+def pytest_sessionstart(session):
+    """The tests load the in-tree libdap.so as built; when none is built yet
+    (a fresh checkout), build it once before anything loads it."""
+    lib = os.path.join(ROOT, "decoder_attention_paged_amd", "libdap.so")
+    if not os.path.exists(lib):
+        from decoder_attention_paged_amd.build import build
+        build(verbose=False)
+
+
 def pytest_configure(config):
     config.addinivalue_line("markers", "gpu: needs an MI355X (runs through the HIP C-ABI library)")
     config.addinivalue_line("markers", "slow: larger CPU oracle cases")
